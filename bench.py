@@ -1,0 +1,177 @@
+#!/usr/bin/env python3
+"""Benchmark of the routed-expert MoE layer at Kimi-K2 shapes on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--config NAME] [--gpus 1]
+
+One step is one pass of the whole layer over one batch already resident in HBM:
+moe_dispatch -> moe_grouped_swiglu (activation quantisation, grouped FP8 gate|up
+GEMM with the fused silu*up requantisation, grouped FP8 down GEMM) -> moe_combine,
+plus the shared expert when the workload has one. W untimed warm-up steps, then K
+timed steps between two device synchronisations. Prints one JSON line.
+
+The dominant kernel (the grouped gate|up GEMM: two thirds of the weight bytes and
+flops) is timed live with HIP events the library records on its launch stream;
+its algorithmic bytes per launch are the gate and up weights and block scales of
+every expert the batch touches, plus the quantised activations it reads and the
+quantised product it writes.
+
+The CPU baseline is the plain oracle (test infrastructure) on a bounded sample of
+the same batch, on this host's cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+FP8_PEAK_TFLOPS = 5000.0       # MI355X dense FP8 matrix peak (no sparsity)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="k2_decode_256")
+    ap.add_argument("--cpu-tokens", type=int, default=None,
+                    help="tokens in the oracle's CPU-baseline sample (default: whole batch up to 256)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this layer is built and measured on a single MI355X "
+              "(no sharding or collectives); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import mixture_experts_ffn_ids_amd as moe
+    from workloads import config_by_name, make_routing, make_x_bits
+    from workloads.gen import make_experts_device, make_shared_device
+
+    if not torch.cuda.is_available():
+        print("no GPU available", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    cfg = config_by_name(args.config)
+
+    # ---- inputs, resident in HBM before timing
+    x_bits = make_x_bits(cfg)
+    ids, w = make_routing(cfg)
+    x = torch.from_numpy(x_bits.view(np.int16)).view(torch.bfloat16).to(dev)
+    t_ids = torch.from_numpy(ids).to(dev)
+    t_w = torch.from_numpy(w).to(dev)
+    experts = make_experts_device(cfg, dev)
+    shared = make_shared_device(cfg, dev) if cfg.shared else None
+    torch.cuda.synchronize()
+
+    def step():
+        return moe.moe_layer(x, t_ids, t_w, experts, shared)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    moe.profile_reset()
+    moe.profile_enable(True)
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(args.steps):
+        out = step()
+    end.record()
+    torch.cuda.synchronize()
+    moe.profile_enable(False)
+    total_ms = start.elapsed_time(end)
+    ms_per_step = total_ms / args.steps
+
+    per_kernel = {}
+    for name, kind in (("quant", moe.KERNEL_QUANT), ("dispatch", moe.KERNEL_DISPATCH),
+                       ("gate_up", moe.KERNEL_GATE_UP), ("down", moe.KERNEL_DOWN),
+                       ("combine", moe.KERNEL_COMBINE)):
+        ms, n = moe.profile_read(kind)
+        per_kernel[name] = {"total_ms": round(ms, 4), "launches": n, "avg_ms": round(ms / n, 5) if n else None}
+
+    # ---- algorithmic work
+    N, d, d_ff, E, K = cfg.N, cfg.d, cfg.d_ff, cfg.E, cfg.K
+    touched = int((np.bincount(ids.ravel(), minlength=E) > 0).sum())
+    n_sh = 1 if cfg.shared else 0
+    w_proj = d * d_ff                                   # bytes of one fp8 projection
+    s_proj = (d // 128) * (d_ff // 128) * 4             # its block scales
+    # gate|up launches: one for the routed experts (+ one for the shared expert)
+    gu_bytes_routed = touched * 2 * (w_proj + s_proj) + N * d + N * (d // 128) * 4 + N * K * d_ff + N * K * (d_ff // 128) * 4
+    gu_bytes_shared = n_sh * (2 * (w_proj + s_proj) + N * d + N * (d // 128) * 4 + N * d_ff + N * (d_ff // 128) * 4)
+    gu_launches_per_step = 1 + n_sh
+    gu_bytes_per_launch = (gu_bytes_routed + gu_bytes_shared) / gu_launches_per_step
+    gu_flops_per_launch = 2.0 * 2 * d * d_ff * (N * K + n_sh * N) / gu_launches_per_step
+    gu = per_kernel["gate_up"]
+    gu_avg_s = gu["avg_ms"] / 1e3
+    achieved_gbs = gu_bytes_per_launch / gu_avg_s / 1e9
+    achieved_tflops = gu_flops_per_launch / gu_avg_s / 1e12
+    layer_bytes = (touched + n_sh) * 3 * (w_proj + s_proj) + 4 * N * d + 8 * N * K
+    layer_flops = 2.0 * 3 * d * d_ff * (N * K + n_sh * N)
+
+    tokens_per_s = N / (ms_per_step / 1e3)
+    result = {
+        "metric": "MoE-layer tokens/s at K2 shapes",
+        "value": round(tokens_per_s, 2),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8-e4m3 x fp8-e4m3 -> fp32 (bf16 in/out)",
+        "data": "synthetic (seeded; random-init fp8 expert weights, 128x128 block scales)",
+        "config": {"workload": cfg.name, "tokens": N, "d": d, "d_ff": d_ff, "experts": E, "top_k": K,
+                   "shared_expert": bool(cfg.shared), "experts_touched": touched},
+        "roofline": {"bound": "hbm", "kernel": "grouped gate|up GEMM (+silu*up requant)",
+                     "achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "algorithmic_bytes_per_launch": int(gu_bytes_per_launch),
+                     "avg_launch_ms": gu["avg_ms"]},
+        "layer": {"hbm_frac": round(layer_bytes / (ms_per_step / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+                  "fp8_mfma_frac": round(layer_flops / (ms_per_step / 1e3) / 1e12 / FP8_PEAK_TFLOPS, 4),
+                  "algorithmic_bytes": int(layer_bytes), "algorithmic_flops": layer_flops,
+                  "gate_up_fp8_mfma_frac": round(achieved_tflops / FP8_PEAK_TFLOPS, 4)},
+        "kernels": per_kernel,
+    }
+
+    # ---- CPU baseline: the oracle as it stands, on a bounded sample of the same batch
+    if not args.no_cpu_baseline:
+        import oracle
+        from workloads.gen import experts_to_host
+        n_cpu = args.cpu_tokens or min(N, 256)
+        tok = np.arange(n_cpu, dtype=np.int64)
+        exh = experts_to_host(experts, np.unique(ids[tok]))
+        shh = experts_to_host(shared) if shared is not None else None
+        threads = len(os.sched_getaffinity(0))
+        threads = min(threads, 16)
+        used = oracle.threads_used(threads)
+        t0 = time.perf_counter()
+        oracle.moe_forward(x_bits, ids, w, exh, shh, tokens=tok, threads=threads)
+        dt = time.perf_counter() - t0
+        result["cpu_baseline"] = {"value": round(n_cpu / dt, 3), "unit": "tokens/s", "cores": used,
+                                  "kind": "oracle",
+                                  "sample": f"first {n_cpu} of {N} tokens of the same batch, {dt:.1f} s"}
+    del out
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

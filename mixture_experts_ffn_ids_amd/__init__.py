@@ -1,0 +1,13 @@
+"""MI355X-native routed-expert MoE layer (Kimi-K2 shapes): Python binding of libmoe.
+
+The layer runs entirely in the HIP kernels of libmoe.so (include/moe.h):
+dispatch -> grouped FP8 SwiGLU experts -> deterministic weighted combine.
+"""
+from .api import (Dispatch, combine, dispatch, grouped_swiglu, identity_dispatch, moe_layer,  # noqa: F401
+                  profile_enable, profile_read, profile_reset, quantize_rows)
+from ._lib import (FLAG_CHECKED, FLAG_TILE_LARGE, FLAG_TILE_MEDIUM, FLAG_TILE_SMALL, KERNEL_COMBINE,  # noqa: F401
+                   KERNEL_DISPATCH, KERNEL_DOWN, KERNEL_GATE_UP, KERNEL_QUANT, LIB_PATH, MoeError)
+
+__all__ = ["Dispatch", "combine", "dispatch", "grouped_swiglu", "identity_dispatch", "moe_layer",
+           "quantize_rows", "profile_enable", "profile_read", "profile_reset", "MoeError", "LIB_PATH",
+           "FLAG_CHECKED", "FLAG_TILE_SMALL", "FLAG_TILE_MEDIUM", "FLAG_TILE_LARGE"]

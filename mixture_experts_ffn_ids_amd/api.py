@@ -1,0 +1,183 @@
+"""Python binding of libmoe: the same calls as include/moe.h, taking torch tensors.
+
+Argument marshalling only -- every step of the layer runs in the HIP kernels of
+libmoe. PyTorch provides device memory (outputs and workspaces are torch
+allocations) and the stream (the current torch stream of the tensors' device).
+
+Layouts (row-major, on one GPU):
+    x          [N, d]       torch.bfloat16
+    topk_ids   [N, K]       torch.int32
+    topk_w     [N, K]       torch.float32
+    experts    object with w_gate, w_up [E, d_ff, d] uint8 (e4m3 codes),
+               s_gate, s_up [E, d_ff/128, d/128] float32,
+               w_down [E, d, d_ff] uint8, s_down [E, d/128, d_ff/128] float32
+"""
+from __future__ import annotations
+
+import ctypes
+from dataclasses import dataclass
+
+import torch
+
+from ._lib import (FLAG_CHECKED, FLAG_TILE_LARGE, FLAG_TILE_MEDIUM, FLAG_TILE_SMALL,  # noqa: F401
+                   KERNEL_COMBINE, KERNEL_DISPATCH, KERNEL_DOWN, KERNEL_GATE_UP, KERNEL_QUANT, check, lib)
+
+
+def _p(t: torch.Tensor | None):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(dev: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _want(t: torch.Tensor, dtype, name: str, ndim: int | None = None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on a GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
+
+
+_WS_CACHE: dict = {}
+
+
+def _workspace(nbytes: int, dev: torch.device, tag: str) -> torch.Tensor:
+    """A cached uint8 workspace per (device, purpose), grown as needed. Calls that use the
+    same workspace are ordered on the current stream."""
+    key = (str(dev), tag)
+    ws = _WS_CACHE.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
+        _WS_CACHE[key] = ws
+    return ws
+
+
+@dataclass
+class Dispatch:
+    counts: torch.Tensor        # [E] int32 (tokens per expert)
+    offsets: torch.Tensor       # [E+1] int32
+    sorted_slot: torch.Tensor   # [N*K] int32, position -> slot
+    slot_pos: torch.Tensor      # [N*K] int32, slot -> position
+    N: int
+    K: int
+    E: int
+
+
+def quantize_rows(x: torch.Tensor):
+    """bf16 rows -> (e4m3 codes uint8 [rows, cols], scales float32 [rows, cols/128])."""
+    _want(x, torch.bfloat16, "x", 2)
+    rows, cols = x.shape
+    q = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
+    s = torch.empty((rows, max(cols // 128, 0)), dtype=torch.float32, device=x.device)
+    check(lib().moe_quantize_rows(_p(x), rows, cols, _p(q), _p(s), _stream(x.device)), "moe_quantize_rows")
+    return q, s
+
+
+def dispatch(topk_ids: torch.Tensor, E: int, checked: bool = False) -> Dispatch:
+    _want(topk_ids, torch.int32, "topk_ids", 2)
+    N, K = topk_ids.shape
+    dev = topk_ids.device
+    counts = torch.empty(E, dtype=torch.int32, device=dev)
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    sorted_slot = torch.empty(N * K, dtype=torch.int32, device=dev)
+    slot_pos = torch.empty(N * K, dtype=torch.int32, device=dev)
+    nb = lib().moe_dispatch_workspace_size(N, K, E)
+    ws = _workspace(nb, dev, "dispatch")
+    st = lib().moe_dispatch(_p(topk_ids), N, K, E, _p(counts), _p(offsets), _p(sorted_slot), _p(slot_pos),
+                            _p(ws), ws.numel(), FLAG_CHECKED if checked else 0, _stream(dev))
+    check(st, "moe_dispatch")
+    return Dispatch(counts, offsets, sorted_slot, slot_pos, N, K, E)
+
+
+def identity_dispatch(N: int, device) -> Dispatch:
+    """Dispatch of every token to a single expert (E = 1, K = 1): the shared expert's rows."""
+    return dispatch(torch.zeros((N, 1), dtype=torch.int32, device=device), 1)
+
+
+def grouped_swiglu(x: torch.Tensor, disp: Dispatch, experts, flags: int = 0,
+                   out: torch.Tensor | None = None) -> torch.Tensor:
+    """y_sorted [N*K, d] bf16: each sorted row through its expert's SwiGLU MLP (unweighted)."""
+    _want(x, torch.bfloat16, "x", 2)
+    N, d = x.shape
+    ex = experts
+    for name in ("w_gate", "w_up", "w_down"):
+        _want(getattr(ex, name), torch.uint8, name, 3)
+    for name in ("s_gate", "s_up", "s_down"):
+        _want(getattr(ex, name), torch.float32, name, 3)
+    E, d_ff, d_w = ex.w_gate.shape
+    if d_w != d or disp.N != N or disp.E != E:
+        raise ValueError("x, dispatch and expert weights disagree on N, d or E")
+    if tuple(ex.w_up.shape) != (E, d_ff, d) or tuple(ex.w_down.shape) != (E, d, d_ff):
+        raise ValueError("expert weight shapes disagree")
+    if (tuple(ex.s_gate.shape) != (E, d_ff // 128, d // 128) or tuple(ex.s_up.shape) != (E, d_ff // 128, d // 128)
+            or tuple(ex.s_down.shape) != (E, d // 128, d_ff // 128)):
+        raise ValueError("expert scale shapes disagree")
+    K = disp.K
+    if out is None:
+        out = torch.empty((N * K, d), dtype=torch.bfloat16, device=x.device)
+    else:
+        _want(out, torch.bfloat16, "out", 2)
+    nb = lib().moe_swiglu_workspace_size(N, K, E, d, d_ff)
+    ws = _workspace(nb, x.device, "swiglu")
+    st = lib().moe_grouped_swiglu(_p(x), N, K, E, d, d_ff, _p(disp.offsets), _p(disp.sorted_slot),
+                                  _p(ex.w_gate), _p(ex.s_gate), _p(ex.w_up), _p(ex.s_up), _p(ex.w_down),
+                                  _p(ex.s_down), _p(out), _p(ws), ws.numel(), int(flags), _stream(x.device))
+    check(st, "moe_grouped_swiglu")
+    return out
+
+
+def combine(y_sorted: torch.Tensor, disp: Dispatch, topk_w: torch.Tensor,
+            shared: torch.Tensor | None = None, out: torch.Tensor | None = None) -> torch.Tensor:
+    """out [N, d] bf16 = sum_k w[n,k] * y_sorted[slot_pos[n*K+k]] (+ shared[n])."""
+    _want(y_sorted, torch.bfloat16, "y_sorted", 2)
+    _want(topk_w, torch.float32, "topk_w", 2)
+    N, K = topk_w.shape
+    d = y_sorted.shape[1]
+    if disp.N != N or disp.K != K or y_sorted.shape[0] != N * K:
+        raise ValueError("combine shapes disagree")
+    if shared is not None:
+        _want(shared, torch.bfloat16, "shared", 2)
+        if tuple(shared.shape) != (N, d):
+            raise ValueError("shared must be [N, d]")
+    if out is None:
+        out = torch.empty((N, d), dtype=torch.bfloat16, device=y_sorted.device)
+    st = lib().moe_combine(_p(y_sorted), _p(disp.slot_pos), _p(topk_w), _p(shared), N, K, d, _p(out),
+                           _stream(y_sorted.device))
+    check(st, "moe_combine")
+    return out
+
+
+def moe_layer(x: torch.Tensor, topk_ids: torch.Tensor, topk_w: torch.Tensor, experts,
+              shared_expert=None, flags: int = 0) -> torch.Tensor:
+    """The whole layer: dispatch -> grouped SwiGLU experts -> weighted combine (+ shared expert)."""
+    E = experts.w_gate.shape[0]
+    disp = dispatch(topk_ids, E)
+    y = grouped_swiglu(x, disp, experts, flags)
+    shared = None
+    if shared_expert is not None:
+        sdisp = identity_dispatch(x.shape[0], x.device)
+        shared = grouped_swiglu(x, sdisp, shared_expert)
+    return combine(y, disp, topk_w, shared)
+
+
+# ---------------------------------------------------------------- profiling
+def profile_enable(on: bool = True):
+    check(lib().moe_profile_enable(1 if on else 0), "moe_profile_enable")
+
+
+def profile_reset():
+    check(lib().moe_profile_reset(), "moe_profile_reset")
+
+
+def profile_read(kind: int):
+    """(total milliseconds, launches) of one kernel kind since the last reset."""
+    ms = ctypes.c_double(0)
+    n = ctypes.c_int64(0)
+    check(lib().moe_profile_read(kind, ctypes.byref(ms), ctypes.byref(n)), "moe_profile_read")
+    return ms.value, n.value

@@ -1,0 +1,65 @@
+"""Build libmoe.so (the HIP library behind include/moe.h) for gfx950, in-tree.
+
+    python -m mixture_experts_ffn_ids_amd.build
+
+Each csrc/*.hip file is compiled to an object with hipcc (in parallel), then
+linked into mixture_experts_ffn_ids_amd/libmoe.so. Packed-FP32 instructions are
+disabled (-packed-fp32-ops); there is no fast-math, so float division and
+square root stay IEEE-correct.
+"""
+from __future__ import annotations
+
+import concurrent.futures as cf
+import os
+import shutil
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+BUILD = os.path.join(PKG, "_build")
+LIB = os.path.join(PKG, "libmoe.so")
+SOURCES = ["api.hip", "quant.hip", "dispatch.hip", "gemm.hip", "combine.hip"]
+ARCH = "gfx950"
+
+
+def hipcc() -> str:
+    for cand in (shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found (ROCm is required to build libmoe)")
+
+
+def common_flags() -> list[str]:
+    return [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
+            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            "-I", os.path.join(ROOT, "include"), "-I", CSRC]
+
+
+def _compile(src: str) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+    cmd = [hipcc(), *common_flags(), "-c", os.path.join(CSRC, src), "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")
+    return obj
+
+
+def build(jobs: int | None = None) -> str:
+    """Compile every HIP source and link libmoe.so. Always rebuilds."""
+    jobs = jobs or min(len(SOURCES), max(1, (os.cpu_count() or 4)))
+    with cf.ThreadPoolExecutor(jobs) as ex:
+        objs = list(ex.map(_compile, SOURCES))
+    tmp = LIB + ".tmp"
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(int(sys.argv[1]) if len(sys.argv) > 1 else None))

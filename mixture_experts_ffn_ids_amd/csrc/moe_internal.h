@@ -1,0 +1,109 @@
+// Internal declarations shared by the HIP sources of libmoe (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+constexpr int kGroup = 128;          // quantisation block edge (weight_block_size 128 x 128)
+constexpr int kMaxTopK = 64;         // MOE_MAX_TOPK
+constexpr float kE4m3Max = 448.0f;   // largest finite OCP e4m3 magnitude
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------- number formats
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
+    return __uint_as_float(bits16 << 16);
+}
+
+// float -> bfloat16 bits, nearest-even (finite inputs; NaN maps to a quiet NaN).
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+// Two floats -> two OCP e4m3 codes (nearest-even) in the low 16 bits; inputs are
+// clamped to +-448 first so that out-of-range values saturate.
+__device__ __forceinline__ uint32_t f32x2_to_e4m3(float a, float b) {
+    a = __builtin_fminf(__builtin_fmaxf(a, -kE4m3Max), kE4m3Max);
+    b = __builtin_fminf(__builtin_fmaxf(b, -kE4m3Max), kE4m3Max);
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false) & 0xffffu;
+}
+
+// Per-group scale from the group's largest magnitude: amax/448, or 1 for a zero group.
+__device__ __forceinline__ float group_scale(float amax) {
+    return amax > 0.0f ? amax / kE4m3Max : 1.0f;
+}
+
+// 16x16x128 FP8 x FP8 -> FP32 matrix core op with unit block scales (E8M0 127 = 2^0).
+// Lane l supplies row (l & 15) of A and column (l & 15) of B, 32 K-values each;
+// the result holds D[4*(l>>4) + i][l & 15] in element i.
+__device__ __forceinline__ v4f mfma_16x16x128_fp8(const v8i& a, const v8i& b) {
+    const v4f zero = {0.f, 0.f, 0.f, 0.f};
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, zero, 0, 0, 0, 127, 0, 127);
+}
+
+// ---------------------------------------------------------------- launchers
+struct GemmPlan;
+
+hipError_t launch_quantize_rows(const uint16_t* x, int64_t rows, int cols, uint8_t* q, float* s,
+                                hipStream_t stream);
+
+constexpr int kDispatchChunk = 256;
+hipError_t launch_dispatch(const int32_t* ids, int64_t N, int K, int E, int32_t* counts,
+                           int32_t* offsets, int32_t* sorted_slot, int32_t* slot_pos,
+                           int32_t* chunk_counts, int32_t* err_flag, bool checked,
+                           hipStream_t stream);
+
+// Tile list: one entry per (expert, block of up to BM sorted rows).
+struct Tile {
+    int32_t expert;
+    int32_t row_begin;
+    int32_t row_end;
+    int32_t pad;
+};
+
+int64_t max_tiles(int64_t rows, int E, int BM);
+
+hipError_t launch_build_tiles(const int32_t* offsets, int E, int64_t rows, int BM, int64_t max_tiles,
+                              Tile* tiles, int32_t* num_tiles, hipStream_t stream);
+
+enum class TileShape { Small = 0, Medium = 1, Large = 2 };
+int tile_rows(TileShape shape);   // BM of the gate|up and down kernels for this shape
+
+struct GateUpArgs {
+    const uint8_t* xq;      // [N][d] e4m3
+    const float* xs;        // [N][d/128]
+    const int32_t* sorted_slot;
+    int64_t N;
+    int K;
+    int64_t rows;           // N*K
+    int d, d_ff;
+    const uint8_t* wg; const float* sg;
+    const uint8_t* wu; const float* su;
+    const Tile* tiles; const int32_t* num_tiles; int64_t max_tiles;
+    uint8_t* hq;            // [rows][d_ff]
+    float* hs;              // [rows][d_ff/128]
+};
+
+struct DownArgs {
+    const uint8_t* hq; const float* hs;
+    int64_t rows;
+    int d, d_ff;
+    const uint8_t* wd; const float* sd;
+    const Tile* tiles; const int32_t* num_tiles; int64_t max_tiles;
+    uint16_t* y;            // [rows][d] bf16
+};
+
+hipError_t launch_gate_up(const GateUpArgs& a, TileShape shape, hipStream_t stream);
+hipError_t launch_down(const DownArgs& a, TileShape shape, hipStream_t stream);
+
+hipError_t launch_combine(const uint16_t* y, const int32_t* slot_pos, const float* w,
+                          const uint16_t* shared, int64_t N, int K, int d, uint16_t* out,
+                          hipStream_t stream);
+
+}  // namespace moe

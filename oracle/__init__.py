@@ -70,6 +70,8 @@ def _load():
                                         P, P, P, P, P, P,
                                         P, P, P, P, P, P, i32,
                                         P, i64, P, P, i32]
+        lib.orc_expert_rows.restype = ctypes.c_int
+        lib.orc_expert_rows.argtypes = [P, i64, i32, i32, i32, P, P, P, P, P, P, P, P, i64, P, P, P, i32]
         lib.orc_threads.restype = ctypes.c_int
         lib.orc_threads.argtypes = [i32]
         _lib = lib
@@ -220,6 +222,25 @@ def moe_forward(x_bits: np.ndarray, ids: np.ndarray, w: np.ndarray, experts: Exp
                                  _ptr(tokens), n_eval, _ptr(out), _ptr(out64), int(threads))
     _check(rc)
     return out, out64
+
+
+def expert_rows(x_bits: np.ndarray, experts, tokens: np.ndarray, expert_ids: np.ndarray,
+                threads: int = 0):
+    """One expert on one token per row: (y float64 [n, d], h codes uint8 [n, d_ff],
+    h scales float32 [n, d_ff/128]) for the pairs (tokens[i], expert_ids[i])."""
+    x_bits = np.ascontiguousarray(x_bits, dtype=np.uint16)
+    N, d = x_bits.shape
+    ex = experts
+    tokens = np.ascontiguousarray(tokens, dtype=np.int64)
+    expert_ids = np.ascontiguousarray(expert_ids, dtype=np.int32)
+    n = tokens.size
+    y = np.empty((n, d), np.float64)
+    hq = np.empty((n, ex.d_ff), np.uint8)
+    hs = np.empty((n, ex.d_ff // GROUP), np.float32)
+    arrs = [np.ascontiguousarray(a) for a in (ex.w_gate, ex.s_gate, ex.w_up, ex.s_up, ex.w_down, ex.s_down)]
+    _check(_load().orc_expert_rows(_ptr(x_bits), N, d, ex.E, ex.d_ff, *[_ptr(a) for a in arrs],
+                                   _ptr(tokens), _ptr(expert_ids), n, _ptr(y), _ptr(hq), _ptr(hs), int(threads)))
+    return y, hq, hs
 
 
 def threads_used(threads: int = 0) -> int:

@@ -390,6 +390,76 @@ int orc_moe_forward(const uint16_t* x, int64_t N, int32_t d, const int32_t* ids,
     return err;
 }
 
+/* ---------------------------------------------------------------------
+ * Single expert rows: for each pair (tokens[i], experts[i]) evaluate the
+ * expert on the quantised token and return y (double, before any rounding)
+ * and, if the pointers are non-NULL, the e4m3 codes and scales of the
+ * requantised product h. Layouts as in orc_moe_forward.
+ * y[n_rows][d], hq[n_rows][d_ff], hs[n_rows][d_ff/128].
+ * ------------------------------------------------------------------- */
+int orc_expert_rows(const uint16_t* x, int64_t N, int32_t d, int32_t E, int32_t d_ff,
+                    const uint8_t* wg, const float* sg, const uint8_t* wu, const float* su,
+                    const uint8_t* wd, const float* sd, const int64_t* tokens,
+                    const int32_t* experts, int64_t n_rows, double* y, uint8_t* hq_out,
+                    float* hs_out, int32_t n_threads)
+{
+    if (N < 0 || d <= 0 || d % GROUP || E < 1 || d_ff <= 0 || d_ff % GROUP || n_rows < 0)
+        return ORC_ERR_SHAPE;
+    for (int64_t i = 0; i < n_rows; ++i) {
+        if (tokens[i] < 0 || tokens[i] >= N)
+            return ORC_ERR_SHAPE;
+        if (experts[i] < 0 || experts[i] >= E)
+            return ORC_ERR_BAD_ID;
+    }
+    double lut[256];
+    for (int c = 0; c < 256; ++c)
+        lut[c] = orc_e4m3_decode((uint8_t)c);
+    const int64_t D = d, F = d_ff;
+    const int64_t ex_w = F * D, ex_s = (F / GROUP) * (D / GROUP);
+    int err = ORC_OK;
+#ifdef _OPENMP
+    if (n_threads > 0)
+        omp_set_num_threads(n_threads);
+#pragma omp parallel
+#endif
+    {
+        double* xdec = (double*)malloc(sizeof(double) * D);
+        float* xs = (float*)malloc(sizeof(float) * (D / GROUP));
+        uint8_t* xq = (uint8_t*)malloc(D);
+        double* g = (double*)malloc(sizeof(double) * F);
+        double* u = (double*)malloc(sizeof(double) * F);
+        float* h = (float*)malloc(sizeof(float) * F);
+        uint8_t* hq = (uint8_t*)malloc(F);
+        float* hs = (float*)malloc(sizeof(float) * (F / GROUP));
+        double* hdec = (double*)malloc(sizeof(double) * F);
+        if (!xdec || !xs || !xq || !g || !u || !h || !hq || !hs || !hdec) {
+#ifdef _OPENMP
+#pragma omp critical
+#endif
+            err = ORC_ERR_NOMEM;
+        } else {
+#ifdef _OPENMP
+#pragma omp for schedule(dynamic, 1)
+#endif
+            for (int64_t i = 0; i < n_rows; ++i) {
+                int64_t e = experts[i];
+                orc_quant_rows_bf16(x + tokens[i] * D, 1, D, xq, xs);
+                for (int64_t j = 0; j < D; ++j)
+                    xdec[j] = lut[xq[j]];
+                expert_forward(xdec, xs, D, F, wg + e * ex_w, sg + e * ex_s, wu + e * ex_w,
+                               su + e * ex_s, wd + e * ex_w, sd + e * ex_s, lut, g, u, h, hq, hs,
+                               hdec, y + i * D);
+                if (hq_out)
+                    memcpy(hq_out + i * F, hq, F);
+                if (hs_out)
+                    memcpy(hs_out + i * (F / GROUP), hs, sizeof(float) * (F / GROUP));
+            }
+        }
+        free(xdec); free(xs); free(xq); free(g); free(u); free(h); free(hq); free(hs); free(hdec);
+    }
+    return err;
+}
+
 /* Threads an OpenMP parallel region gets with the given request (for the
  * benchmark's report of the cores the oracle used). */
 int orc_threads(int32_t n_threads)

@@ -27,3 +27,15 @@ def pytest_collection_modifyitems(config, items):
     for item in items:
         if "gpu" in item.keywords:
             item.add_marker(skip)
+
+
+@pytest.fixture(scope="session", autouse=True)
+def _built_libraries():
+    """Build the oracle and libmoe.so once if they are missing (tests never rebuild what exists)."""
+    import oracle
+    from mixture_experts_ffn_ids_amd import build as moe_build
+    if not os.path.exists(os.path.join(ROOT, "oracle", "liboracle.so")):
+        oracle.build(force=False)
+    if not os.path.exists(moe_build.LIB):
+        moe_build.build()
+    yield

@@ -1,0 +1,56 @@
+"""GPU: moe_quantize_rows (the activation quantiser, first step of the grouped SwiGLU
+call) must match the oracle bit for bit -- codes and scales."""
+import numpy as np
+import pytest
+import torch
+
+import mixture_experts_ffn_ids_amd as moe
+import oracle
+from parity import bf16_dev, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _rows(rng, rows, cols):
+    x = rng.standard_normal((rows, cols)).astype(np.float32)
+    x *= np.exp2(rng.integers(-20, 20, (rows, 1))).astype(np.float32)
+    if rows > 2:
+        x[1, :128] = 0.0                       # zero group -> scale 1
+        x[2, 128 % cols:128 % cols + 128] = -0.0
+    if rows > 3:
+        x[3, ::7] *= 1e-30                     # values deep in e4m3's subnormal range after scaling
+    return torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+@pytest.mark.parametrize("rows,cols", [(1, 128), (5, 256), (37, 7168), (1000, 2048), (3, 384)])
+def test_quantize_rows_bit_exact(rows, cols):
+    rng = np.random.default_rng(rows * 131 + cols)
+    bits = _rows(rng, rows, cols)
+    say(f"quantize rows={rows} cols={cols}")
+    q, s = moe.quantize_rows(bf16_dev(bits))
+    torch.cuda.synchronize()
+    q_ref, s_ref = oracle.quant_rows_bf16(bits)
+    assert np.array_equal(s.cpu().numpy().view(np.uint32), s_ref.view(np.uint32))
+    assert np.array_equal(q.cpu().numpy(), q_ref)
+
+
+def test_e4m3_conversion_exhaustive_over_bf16():
+    """Every finite bf16 value v with |v| <= 448, placed in a group whose amax is 448
+    (scale exactly 1), so the code is the conversion of v itself."""
+    allb = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    vals = oracle.bf16_to_f32(allb)
+    keep = np.isfinite(vals) & (np.abs(vals) <= 448.0)
+    v = allb[keep]
+    per = 127
+    ngroups = (v.size + per - 1) // per
+    pad = ngroups * per - v.size
+    v = np.concatenate([v, np.zeros(pad, np.uint16)]).reshape(ngroups, per)
+    anchor = np.full((ngroups, 1), 0x43E0, np.uint16)    # bf16 448.0
+    bits = np.ascontiguousarray(np.concatenate([anchor, v], axis=1))
+    say(f"e4m3 exhaustive groups={ngroups}")
+    q, s = moe.quantize_rows(bf16_dev(bits))
+    torch.cuda.synchronize()
+    q_ref, s_ref = oracle.quant_rows_bf16(bits)
+    assert np.all(s_ref == 1.0)
+    assert np.array_equal(s.cpu().numpy(), s_ref)
+    assert np.array_equal(q.cpu().numpy(), q_ref)

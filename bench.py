@@ -43,11 +43,55 @@ def parse():
     ap.add_argument("--cpu-tokens", type=int, default=None,
                     help="tokens in the oracle's CPU-baseline sample (default: whole batch up to 256)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="instead of the layer, run a plain device-to-device copy of this many bytes "
+                         "(5 launches): the reference for scaling rocprofv3's HBM byte counters")
     return ap.parse_args()
+
+
+def gemm_source_sha256() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for name in ("gemm.hip", "moe_internal.h"):
+        with open(os.path.join(ROOT, "mixture_experts_ffn_ids_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def stored_traffic(workload: str):
+    """HBM bytes per gate|up launch from the committed rocprofv3 counter summary of this
+    workload (FETCH_SIZE and WRITE_SIZE, scaled by the copy calibration), or None when
+    there is none or the kernel source has changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"gate_up_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    rec = None
+    with open(path) as f:
+        for line in f:
+            if line.startswith("traffic-record:"):
+                rec = dict(kv.split("=", 1) for kv in line.split()[1:])
+    if not rec or rec.get("source_sha256") != gemm_source_sha256():
+        return None
+    kib = float(rec["fetch_kib"]) * float(rec["fetch_scale"]) + float(rec["write_kib"]) * float(rec["write_scale"])
+    return int(kib * 1024)
+
+
+def copy_calibration(nbytes: int):
+    import torch
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": nbytes, "launches": 5}), flush=True)
 
 
 def main():
     args = parse()
+    if args.copy_bytes:
+        copy_calibration(args.copy_bytes)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this layer is built and measured on a single MI355X "
               "(no sharding or collectives); run with --gpus 1", file=sys.stderr)
@@ -142,7 +186,7 @@ def main():
                    "shared_expert": bool(cfg.shared), "experts_touched": touched},
         "roofline": {"bound": "hbm", "kernel": "grouped gate|up GEMM (+silu*up requant)",
                      "achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved_gbs / HBM_PEAK_GBS, 4), "traffic": stored_traffic(cfg.name),
                      "algorithmic_bytes_per_launch": int(gu_bytes_per_launch),
                      "avg_launch_ms": gu["avg_ms"]},
         "layer": {"hbm_frac": round(layer_bytes / (ms_per_step / 1e3) / 1e9 / HBM_PEAK_GBS, 4),

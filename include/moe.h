@@ -69,12 +69,14 @@ typedef enum {
 
 /* Validate expert ids on the device and wait for the result (one host sync). */
 #define MOE_FLAG_CHECKED 1u
-/* moe_grouped_swiglu: force the GEMM tile height instead of choosing it from the
- * expected rows per expert, N*K / min(E, N*K) (results do not depend on it). */
-#define MOE_FLAG_TILE_SMALL (1u << 4)   /* 16 rows per tile  */
-#define MOE_FLAG_TILE_MEDIUM (2u << 4)  /* 64 rows per tile  */
-#define MOE_FLAG_TILE_LARGE (3u << 4)   /* 128 rows per tile */
-#define MOE_FLAG_TILE_MASK (3u << 4)
+/* moe_grouped_swiglu: force the GEMM tile height (sorted rows of one expert per
+ * workgroup) instead of choosing it from the expected rows per expert,
+ * N*K / min(E, N*K). Results do not depend on it, bit for bit. */
+#define MOE_FLAG_TILE_16 (1u << 4)
+#define MOE_FLAG_TILE_128 (2u << 4)
+#define MOE_FLAG_TILE_192 (3u << 4)
+#define MOE_FLAG_TILE_256 (4u << 4)
+#define MOE_FLAG_TILE_MASK (7u << 4)
 
 /* Limits (checked, MOE_ERR_SHAPE beyond them). */
 #define MOE_MAX_EXPERTS 8192

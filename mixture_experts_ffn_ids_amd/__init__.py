@@ -5,9 +5,9 @@ dispatch -> grouped FP8 SwiGLU experts -> deterministic weighted combine.
 """
 from .api import (Dispatch, combine, dispatch, grouped_swiglu, identity_dispatch, moe_layer,  # noqa: F401
                   profile_enable, profile_read, profile_reset, quantize_rows)
-from ._lib import (FLAG_CHECKED, FLAG_TILE_LARGE, FLAG_TILE_MEDIUM, FLAG_TILE_SMALL, KERNEL_COMBINE,  # noqa: F401
+from ._lib import (FLAG_CHECKED, FLAG_TILE_16, FLAG_TILE_128, FLAG_TILE_192, FLAG_TILE_256, KERNEL_COMBINE,  # noqa: F401
                    KERNEL_DISPATCH, KERNEL_DOWN, KERNEL_GATE_UP, KERNEL_QUANT, LIB_PATH, MoeError)
 
 __all__ = ["Dispatch", "combine", "dispatch", "grouped_swiglu", "identity_dispatch", "moe_layer",
            "quantize_rows", "profile_enable", "profile_read", "profile_reset", "MoeError", "LIB_PATH",
-           "FLAG_CHECKED", "FLAG_TILE_SMALL", "FLAG_TILE_MEDIUM", "FLAG_TILE_LARGE"]
+           "FLAG_CHECKED", "FLAG_TILE_16", "FLAG_TILE_128", "FLAG_TILE_192", "FLAG_TILE_256"]

@@ -17,9 +17,10 @@ STATUS_NAMES = {0: "MOE_OK", 1: "MOE_ERR_NULL", 2: "MOE_ERR_SHAPE", 3: "MOE_ERR_
                 8: "MOE_ERR_DEVICE"}
 
 FLAG_CHECKED = 1
-FLAG_TILE_SMALL = 1 << 4
-FLAG_TILE_MEDIUM = 2 << 4
-FLAG_TILE_LARGE = 3 << 4
+FLAG_TILE_16 = 1 << 4
+FLAG_TILE_128 = 2 << 4
+FLAG_TILE_192 = 3 << 4
+FLAG_TILE_256 = 4 << 4
 
 KERNEL_QUANT, KERNEL_DISPATCH, KERNEL_GATE_UP, KERNEL_DOWN, KERNEL_COMBINE = range(5)
 

@@ -5,7 +5,7 @@
 #include <string.h>
 #include <vector>
 
-#include "../../include/moe.h"
+#include "moe.h"
 #include "moe_internal.h"
 
 using namespace moe;
@@ -119,7 +119,7 @@ SwigluWs swiglu_layout(int64_t N, int32_t K, int32_t E, int32_t d, int32_t d_ff)
     w.hq = off; off = align_up(off + (size_t)rows * d_ff);
     w.hs = off; off = align_up(off + (size_t)rows * (d_ff / kGroup) * sizeof(float));
     // sized for the smallest tile height, so every tile shape fits
-    w.tile_cap = max_tiles(rows, E, tile_rows(TileShape::Small));
+    w.tile_cap = max_tiles(rows, E, tile_rows(TileShape::Rows16));
     w.tiles = off; off = align_up(off + (size_t)w.tile_cap * sizeof(Tile));
     w.ntiles = off; off = align_up(off + sizeof(int32_t));
     w.total = off;
@@ -130,16 +130,18 @@ bool dim_ok(int32_t v) { return v > 0 && v % kGroup == 0 && v <= MOE_MAX_DIM; }
 
 TileShape choose_shape(int64_t rows, int32_t E, uint32_t flags) {
     switch (flags & MOE_FLAG_TILE_MASK) {
-        case MOE_FLAG_TILE_SMALL: return TileShape::Small;
-        case MOE_FLAG_TILE_MEDIUM: return TileShape::Medium;
-        case MOE_FLAG_TILE_LARGE: return TileShape::Large;
+        case MOE_FLAG_TILE_16: return TileShape::Rows16;
+        case MOE_FLAG_TILE_128: return TileShape::Rows128;
+        case MOE_FLAG_TILE_192: return TileShape::Rows192;
+        case MOE_FLAG_TILE_256: return TileShape::Rows256;
         default: break;
     }
     const int64_t touched = rows < E ? rows : E;
     const int64_t per = touched > 0 ? rows / touched : 0;  // expected rows per touched expert
-    if (per < 24) return TileShape::Small;
-    if (per < 96) return TileShape::Medium;
-    return TileShape::Large;
+    if (per < 24) return TileShape::Rows16;
+    if (per < 112) return TileShape::Rows128;
+    if (per < 184) return TileShape::Rows192;
+    return TileShape::Rows256;
 }
 
 }  // namespace

@@ -168,16 +168,18 @@ __global__ __launch_bounds__(1024) void k_tiles(const int32_t* __restrict__ offs
         int64_t b = offsets[e], en = offsets[e + 1];
         b = b < 0 ? 0 : (b > rows ? rows : b);
         en = en < b ? b : (en > rows ? rows : en);
+        const int64_t first = t;
+        const int64_t count = (en - b + BM - 1) / BM;
         // stops at the cap, so arbitrary offsets cannot make this loop long
         for (int64_t r = b; r < en && t < cap; r += BM, ++t) {
-            {
-                Tile tl;
-                tl.expert = e;
-                tl.row_begin = (int32_t)r;
-                tl.row_end = (int32_t)(r + BM < en ? r + BM : en);
-                tl.pad = 0;
-                tiles[t] = tl;
-            }
+            Tile tl;
+            tl.expert = e;
+            tl.row_begin = (int32_t)r;
+            tl.row_end = (int32_t)(r + BM < en ? r + BM : en);
+            tl.first = (int32_t)first;
+            tl.count = (int32_t)count;
+            tl.pad[0] = tl.pad[1] = tl.pad[2] = 0;
+            tiles[t] = tl;
         }
     }
     if (threadIdx.x == 0) *num_tiles = (int32_t)(total < cap ? total : cap);

@@ -64,7 +64,6 @@ __device__ __forceinline__ v8i load_frag_lds(const uint8_t* p) {
     return r;
 }
 
-__device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
 
 // MODE 0: gate|up with the silu*up requant epilogue; MODE 1: down with bf16 output.
 template <int MODE, int WM, int WN, int MT, int NT>
@@ -236,7 +235,7 @@ __global__ __launch_bounds__(WM* WN * 64) void k_grouped_gemm(const GemmParams P
                 float m = 0.0f;
 #pragma unroll
                 for (int nt = 0; nt < NT; ++nt) {
-                    const float v = silu(acc[0][mt][nt][i]) * acc[1][mt][nt][i];
+                    const float v = silu_fast(acc[0][mt][nt][i]) * acc[1][mt][nt][i];
                     h[mt][nt][i] = v;
                     m = __builtin_fmaxf(m, __builtin_fabsf(v));
                 }
@@ -288,9 +287,10 @@ __global__ __launch_bounds__(WM* WN * 64) void k_grouped_gemm(const GemmParams P
 // so that one tile list serves both.
 int tile_rows(TileShape shape) {
     switch (shape) {
-        case TileShape::Small: return 16;
-        case TileShape::Medium: return 64;
-        default: return 128;
+        case TileShape::Rows16: return 16;
+        case TileShape::Rows128: return 128;
+        case TileShape::Rows192: return 192;
+        default: return 256;
     }
 }
 
@@ -314,9 +314,8 @@ hipError_t launch_gate_up(const GateUpArgs& a, TileShape shape, hipStream_t stre
     P.tiles = a.tiles; P.num_tiles = a.num_tiles;
     P.hq = a.hq; P.hs = a.hs;
     switch (shape) {
-        case TileShape::Small: return launch<0, 1, 4, 1, 2>(P, a.max_tiles, stream);
-        case TileShape::Medium: return launch<0, 1, 4, 4, 2>(P, a.max_tiles, stream);
-        default: return launch<0, 2, 4, 4, 2>(P, a.max_tiles, stream);
+        case TileShape::Rows16: return launch<0, 1, 4, 1, 2>(P, a.max_tiles, stream);
+        default: return launch_gate_up_lds(a, tile_rows(shape), stream);
     }
 }
 
@@ -328,9 +327,8 @@ hipError_t launch_down(const DownArgs& a, TileShape shape, hipStream_t stream) {
     P.tiles = a.tiles; P.num_tiles = a.num_tiles;
     P.y = a.y;
     switch (shape) {
-        case TileShape::Small: return launch<1, 1, 4, 1, 4>(P, a.max_tiles, stream);
-        case TileShape::Medium: return launch<1, 1, 4, 4, 4>(P, a.max_tiles, stream);
-        default: return launch<1, 2, 4, 4, 4>(P, a.max_tiles, stream);
+        case TileShape::Rows16: return launch<1, 1, 4, 1, 4>(P, a.max_tiles, stream);
+        default: return launch_down_lds(a, tile_rows(shape), stream);
     }
 }
 

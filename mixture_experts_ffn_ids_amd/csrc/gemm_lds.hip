@@ -1,0 +1,464 @@
+// Grouped FP8 GEMMs for tiles of many rows (prefill): both operands staged in LDS by
+// direct global->LDS copies, with a deeper ring for the weights than for the activations.
+//
+// Same mathematics as gemm.hip ("SwiGLU output" page, evidence "mlp"; "Element-wise
+// product" page; FP8 block format from "Input features" page, evidence "linear"):
+//   gate|up: G, U = Xq[rows] . W_gate[e]^T, . W_up[e]^T -> h = silu(G) * U, e4m3 per 128
+//   down:    Y = Hq[rows] . W_down[e]^T -> bf16
+// One v_mfma_scale_f32_16x16x128_f8f6f4 per 128-wide quantisation block; each 16x16
+// partial is multiplied by (row activation scale x weight block scale) and added to the
+// fp32 accumulator.
+//
+// Workgroup: 8 waves (2 along the rows x 4 along the weight rows), 512 threads. It owns
+// one tile (<= BM = 32 MT sorted rows of one expert, MT = 4, 6 or 8) and 256 weight rows:
+// for gate|up the 128 gate and 128 up rows of one 128-wide d_ff block (so the
+// requantisation group is complete), for down 256 output columns. Each wave computes
+// 16 MT rows x 4 weight-row subtiles of 16 (64 columns): MT x 4 MFMA tiles.
+//
+// Data movement per 128-wide K block, all by global_load_lds (lane L of a wave writes its
+// 16 bytes at LDS base + 16 L; no registers involved):
+//   * weights (256 x 128 B) and activations (BM x 128 B, gathered token rows for gate|up)
+//     into rings of 3 stages for 128-row tiles and 2 for larger ones (LDS capacity), so one
+//     or two blocks are in flight while one is multiplied;
+//   * row scales one block earlier than their rows, so that the thread owning a row can
+//     turn them into the products with this workgroup's weight block scales (the factors
+//     the MFMA loop applies) one block ahead, without an extra barrier.
+// Rows are 128 B with 16-B chunks XOR-swizzled so that fragment reads are free of bank
+// conflicts. Rows past the end of the tile copy a valid row (the tile's first row, or the
+// last weight row); they are computed but never stored. The copies are written as inline
+// assembly so that the compiler does not wait for them at every LDS read; completion is
+// awaited explicitly (s_waitcnt vmcnt) before the barrier that publishes a block.
+//
+// Scheduling: workgroups are dispatched round-robin over the 8 XCDs. The workgroup id is
+// remapped so that each XCD gets a contiguous range of (expert, n-block, row tile) items:
+// the row tiles that share a weight block, and the n-blocks that share a tile's rows, run
+// on the same XCD at about the same time and share its L2.
+//
+// Epilogue: results are staged through the (then idle) stage buffers and written with
+// coalesced 16-byte stores.
+#include "moe_internal.h"
+
+namespace moe {
+
+namespace {
+
+constexpr int kXcds = 8;
+constexpr int kOutPitch = 256 + 8;  // bf16 elements per row of the staged down-GEMM output
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+template <int MODE, int MT>
+struct Cfg {
+    static constexpr int NW = 8;                  // waves: 2 along the rows x 4 along the weights
+    static constexpr int THREADS = NW * 64;
+    static constexpr int BM = 32 * MT;            // rows per tile
+    static constexpr int BR = 256;                // weight rows per workgroup
+    static constexpr int A_BYTES = BM * 128;      // one activation stage
+    static constexpr int B_BYTES = BR * 128;      // one weight stage
+    // stages of the activation and weight rings: both three deep where LDS allows (128-row
+    // tiles); otherwise two (measured faster at 192 rows than a three-deep weight ring)
+    static constexpr int NA = BM <= 128 ? 3 : 2;
+    static constexpr int NBS = BM <= 128 ? 3 : 2;
+    static constexpr int A_Q = BM / 64;           // 1-KB wave copies of A per wave per K block
+    static constexpr int B_Q = BR / 64;           // same for B
+    static constexpr int S_Q = BM / 64;           // 256-B copies of row scales (waves 0..S_Q-1)
+    static constexpr int STAGES = NA * A_BYTES + NBS * B_BYTES;
+    static constexpr int OUT_BYTES = MODE == 1 ? BM * kOutPitch * 2 : BM * 128 + 4 * BM * 4;
+    static constexpr int MAIN = STAGES > OUT_BYTES ? STAGES : OUT_BYTES;
+    static constexpr int MAX_KB = 65536 / 128;    // K blocks at the largest supported K
+    // LDS: A stages | B stages (or the output tile) | row scales [3][BM] | factors [2][2][BM]
+    //      | source rows [BM] | weight block scales [2][MAX_KB]
+    static constexpr int LDS = MAIN + 3 * BM * 4 + 4 * BM * 4 + BM * 4 + 2 * MAX_KB * 4;
+    static_assert(A_Q * NW * 64 == BM * 8 && B_Q * NW * 64 == BR * 8, "copy split");
+    static_assert(S_Q <= NW && BM <= THREADS, "scale copies");
+    static_assert(LDS <= 160 * 1024, "LDS budget");
+    static_assert(A_Q + B_Q + 1 <= 15, "pending copies fit the wait helper");
+};
+
+struct LdsGemmParams {
+    const uint8_t* a;          // activation codes, row stride Kdim
+    const float* as;           // activation scales, row stride Kdim/128
+    const int32_t* gather;     // gate|up: sorted_slot; down: NULL
+    int K_top;
+    int64_t src_rows;
+    int Kdim, Ndim;            // Ndim: d_ff (gate|up) or d (down)
+    const uint8_t* w0; const float* s0;
+    const uint8_t* w1; const float* s1;
+    const Tile* tiles; const int32_t* num_tiles;
+    uint8_t* hq; float* hs;
+    uint16_t* y;
+};
+
+// Byte offset of 16-B chunk c of row r in a swizzled [rows][128 B] LDS tile. A fragment read
+// has 16 lanes fetch one logical chunk of 16 consecutive rows; the chunk is placed at
+// c ^ (r & 7) ^ ((r >> 3) & 1), which gives those 16 rows distinct 16-B slots modulo 256 B
+// and each aligned group of 8 rows distinct slots modulo 128 B: no bank conflicts whether
+// the LDS serves 16 lanes over 64 banks or 8 lanes over 32 banks per cycle.
+__device__ __forceinline__ int swz_pos(int r, int c) { return c ^ (r & 7) ^ ((r >> 3) & 1); }
+__device__ __forceinline__ int swz(int r, int c) { return r * 128 + (swz_pos(r, c) << 4); }
+
+__device__ __forceinline__ v8i lds_frag(const uint8_t* tile, int r, int kg) {
+    // 32 K-bytes [32*kg, 32*kg+32) of row r: logical chunks 2kg and 2kg+1
+    const uint4 lo = *reinterpret_cast<const uint4*>(tile + swz(r, 2 * kg));
+    const uint4 hi = *reinterpret_cast<const uint4*>(tile + swz(r, 2 * kg + 1));
+    v8i v;
+    v[0] = lo.x; v[1] = lo.y; v[2] = lo.z; v[3] = lo.w;
+    v[4] = hi.x; v[5] = hi.y; v[6] = hi.z; v[7] = hi.w;
+    return v;
+}
+
+// Global -> LDS copies (global_load_lds): lane L writes its 16 (or 4) bytes at
+// l + 16 L (or 4 L); l must be the same for the whole wave.
+__device__ __forceinline__ uint32_t lds_addr(const void* l) {
+    return __builtin_amdgcn_readfirstlane((uint32_t)(size_t)(lds_ptr_t)(l));
+}
+__device__ __forceinline__ void copy16(const uint8_t* g, uint8_t* l) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_addr(l)), "v"(g)
+                 : "memory", "m0");
+}
+__device__ __forceinline__ void copy4(const float* g, float* l) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off" ::"s"(lds_addr(l)), "v"(g)
+                 : "memory", "m0");
+}
+// wait until at most N of this wave's copies are still in flight (they complete in order)
+template <int N>
+__device__ __forceinline__ void wait_copies() {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+// the same with N known only at run time (uniform over the wave; at most 15 here)
+__device__ __forceinline__ void wait_pending(int n) {
+    switch (n) {
+        case 0: wait_copies<0>(); break;
+        case 1: wait_copies<1>(); break;
+        case 2: wait_copies<2>(); break;
+        case 3: wait_copies<3>(); break;
+        case 4: wait_copies<4>(); break;
+        case 5: wait_copies<5>(); break;
+        case 6: wait_copies<6>(); break;
+        case 7: wait_copies<7>(); break;
+        case 8: wait_copies<8>(); break;
+        case 9: wait_copies<9>(); break;
+        case 10: wait_copies<10>(); break;
+        case 11: wait_copies<11>(); break;
+        case 12: wait_copies<12>(); break;
+        case 13: wait_copies<13>(); break;
+        case 14: wait_copies<14>(); break;
+        default: wait_copies<15>(); break;
+    }
+}
+
+
+template <int MODE, int MT>
+__global__ __launch_bounds__(512) void k_gemm_lds(const LdsGemmParams P) {
+    using C = Cfg<MODE, MT>;
+    constexpr int BM = C::BM, NBS = C::NBS;
+
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    constexpr int NA = C::NA;
+    uint8_t* const sA = smem;                                   // [NA][BM][128]
+    uint8_t* const sB = smem + NA * C::A_BYTES;                 // [NBS][256][128]
+    float* const sSA = reinterpret_cast<float*>(smem + C::MAIN); // [3][BM] row scales
+    float* const sF = sSA + 3 * BM;                             // [2][2][BM] factors
+    int32_t* const sRow = reinterpret_cast<int32_t*>(sF + 4 * BM);  // [BM]
+    float* const sSw = reinterpret_cast<float*>(sRow + BM);     // [2][MAX_KB]
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    // the wave index is uniform within a wave: keep what derives from it in scalar registers
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 2, wn = wave & 3;
+    const int n_blocks = MODE == 0 ? P.Ndim / 128 : (P.Ndim + 255) / 256;
+
+    // ---- XCD-aware work item (expert, n-block, row tile)
+    const int32_t ntile = *P.num_tiles;
+    const int64_t work = (int64_t)ntile * n_blocks;
+    const int64_t per_xcd = (work + kXcds - 1) / kXcds;
+    const int64_t item = (int64_t)(blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
+    if (blockIdx.x / kXcds >= per_xcd || item >= work) return;
+    const Tile head = P.tiles[item / n_blocks];   // a tile of the item's expert
+    const int64_t local = item - (int64_t)n_blocks * head.first;
+    const int nb = (int)(local / head.count);
+    const int t = head.first + (int)(local % head.count);
+    if (t >= ntile) return;
+    const Tile tile = P.tiles[t];
+    const int e = tile.expert;
+    const int64_t p0 = tile.row_begin;
+    const int nrows = tile.row_end - tile.row_begin;
+    const int KB = P.Kdim / 128;
+    const int NB128 = P.Ndim / 128;
+    const int n0 = MODE == 0 ? nb * 128 : nb * 256;
+
+    // source row of every tile row; rows past the end repeat the tile's first row
+    for (int r = tid; r < BM; r += C::THREADS) {
+        const int64_t p = p0 + (r < nrows ? r : 0);
+        int32_t src;
+        if (MODE == 0) {
+            int64_t tok = P.gather[p] / P.K_top;
+            tok = tok < 0 ? 0 : (tok >= P.src_rows ? P.src_rows - 1 : tok);
+            src = (int32_t)tok;
+        } else {
+            src = (int32_t)p;
+        }
+        sRow[r] = src;
+    }
+    // weight block scales of the workgroup's columns for every K block: gate|up -> gate and
+    // up scales of d_ff block nb; down -> the two 128-column blocks of n-block nb
+    for (int i = tid; i < 2 * KB; i += C::THREADS) {
+        const int which = i / KB, kb = i % KB;
+        float v;
+        if (MODE == 0) {
+            v = (which == 0 ? P.s0 : P.s1)[((int64_t)e * NB128 + nb) * KB + kb];
+        } else {
+            const int cb = n0 / 128 + which;
+            v = cb < NB128 ? P.s0[((int64_t)e * NB128 + cb) * KB + kb] : 0.0f;
+        }
+        sSw[which * C::MAX_KB + kb] = v;
+    }
+    __syncthreads();
+
+    // ---- per-lane copy plan. Wave copy q fills rows 8q .. 8q+7 of a stage; lane L lands in
+    // row 8q + (L >> 3), slot L & 7, which holds logical chunk (L & 7) ^ (L >> 3) ^ (q & 1);
+    // all q of a wave (q = wave + i * 8) have the parity of the wave.
+    const int lrow = lane >> 3;
+    const int lchunk = (lane & 7) ^ lrow ^ (wave & 1);
+    uint32_t aRow[C::A_Q];
+#pragma unroll
+    for (int i = 0; i < C::A_Q; ++i) aRow[i] = (uint32_t)sRow[8 * (wave + i * C::NW) + lrow];
+    const uint8_t* bBase[C::B_Q];
+    uint32_t bOff[C::B_Q];
+#pragma unroll
+    for (int i = 0; i < C::B_Q; ++i) {
+        const int q = wave + i * C::NW;
+        const int r = 8 * q + lrow;
+        if (MODE == 0) {
+            bBase[i] = (q < 16 ? P.w0 : P.w1) + (int64_t)e * P.Ndim * P.Kdim;
+            bOff[i] = (uint32_t)(n0 + (r & 127)) * (uint32_t)P.Kdim + lchunk * 16;
+        } else {
+            bBase[i] = P.w0 + (int64_t)e * P.Ndim * P.Kdim;
+            int col = n0 + r;
+            col = col < P.Ndim ? col : P.Ndim - 1;
+            bOff[i] = (uint32_t)col * (uint32_t)P.Kdim + lchunk * 16;
+        }
+    }
+    const uint32_t sOff = wave < C::S_Q ? (uint32_t)sRow[wave * 64 + lane] * (uint32_t)KB : 0u;
+
+    auto issueA = [&](int kb) {
+        uint8_t* A = sA + (kb % NA) * C::A_BYTES;
+        const uint32_t ko = (uint32_t)kb * 128;
+#pragma unroll
+        for (int i = 0; i < C::A_Q; ++i)
+            copy16(P.a + (size_t)aRow[i] * P.Kdim + lchunk * 16 + ko, A + (wave + i * C::NW) * 1024);
+    };
+    auto issueS = [&](int kb) {
+        if (wave < C::S_Q) copy4(P.as + sOff + kb, sSA + (kb % 3) * BM + wave * 64);
+    };
+    auto issueB = [&](int kb) {
+        uint8_t* B = sB + (kb % NBS) * C::B_BYTES;
+        const uint32_t ko = (uint32_t)kb * 128;
+#pragma unroll
+        for (int i = 0; i < C::B_Q; ++i) copy16(bBase[i] + bOff[i] + ko, B + (wave + i * C::NW) * 1024);
+    };
+    // factors of K block kb (its row scales have landed): F[kb & 1][which][row]
+    auto factors = [&](int kb) {
+        if (tid < BM) {
+            const float sa = sSA[(kb % 3) * BM + tid];
+            sF[((kb & 1) * 2 + 0) * BM + tid] = sa * sSw[kb];
+            sF[((kb & 1) * 2 + 1) * BM + tid] = sa * sSw[C::MAX_KB + kb];
+        }
+    };
+
+    // weight-row base (within the B tile) of this wave's 4 subtiles
+    int bbase[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        bbase[j] = MODE == 0 ? (j >> 1) * 128 + wn * 32 + (j & 1) * 16 : wn * 64 + j * 16;
+
+    v4f acc[MT][4];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[mt][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+    // ---- pipeline. Block kb's activations are copied NA-1 iterations ahead, its weights
+    // NBS-1 ahead and its row scales NA ahead (one earlier than its rows, so their factors can
+    // be formed the iteration before the block is used). At the end of iteration kb, block
+    // kb+1 (and the scales of kb+2) must have landed; copies that may still be in flight then
+    // are issued last, so an in-order count of pending copies is an exact wait.
+    const int sq = wave < C::S_Q ? 1 : 0;   // this wave copies one 64-row slice of scales
+    // prologue: everything block 0 and 1's factors need, then the copies that may stay pending
+    issueB(0);
+    issueA(0);
+    issueS(0);
+    if (KB > 1) issueS(1);
+    int pend = 0;
+    if (NA == 3 && KB > 1) { issueA(1); pend += C::A_Q; }
+    if (NBS == 3 && KB > 1) { issueB(1); pend += C::B_Q; }
+    if (NA == 3 && KB > 2) { issueS(2); pend += sq; }
+    wait_pending(pend);
+    __syncthreads();
+    factors(0);
+    __syncthreads();
+
+    const int rlane = lane & 15, kg = lane >> 4;
+    // gate|up: subtiles 0,1 gate and 2,3 up use factor tables 0 and 1; down: the wave's
+    // 64 columns lie in 128-column block wn >> 1
+    const int ftab = MODE == 0 ? 0 : (wn >> 1);
+    for (int kb = 0; kb < KB; ++kb) {
+        // refill the buffers read in iteration kb - 1 (the barrier below separates them);
+        // copies that must land by the end of this iteration first, those that may not, last
+        const bool iA = kb + NA - 1 < KB, iB = kb + NBS - 1 < KB, iS = kb + NA < KB;
+        int pend_end = 0;
+        if (NA == 2 && NBS == 2) {
+            if (iB) issueB(kb + 1);
+            if (iA) issueA(kb + 1);
+            if (iS) issueS(kb + 2);
+        } else if (NA == 2) {      // NBS == 3: only the weights may stay in flight
+            if (iA) issueA(kb + 1);
+            if (iS) issueS(kb + 2);
+            if (iB) { issueB(kb + 2); pend_end = C::B_Q; }
+        } else {                   // NA == NBS == 3: all of this iteration's copies may
+            if (iB) { issueB(kb + 2); pend_end += C::B_Q; }
+            if (iA) { issueA(kb + 2); pend_end += C::A_Q; }
+            if (iS) { issueS(kb + 3); pend_end += sq; }
+        }
+        if (kb + 1 < KB) factors(kb + 1);
+
+        const uint8_t* A = sA + (kb % NA) * C::A_BYTES;
+        const uint8_t* B = sB + (kb % NBS) * C::B_BYTES;
+        const float* F = sF + (kb & 1) * 2 * BM;
+        v8i bf[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) bf[j] = lds_frag(B, bbase[j] + rlane, kg);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            const int rb = wm * MT * 16 + mt * 16;
+            const v8i af = lds_frag(A, rb + rlane, kg);
+            const float4 f0 = *reinterpret_cast<const float4*>(F + ftab * BM + rb + 4 * kg);
+            const float4 f1 = MODE == 0 ? *reinterpret_cast<const float4*>(F + BM + rb + 4 * kg) : f0;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const v4f r = mfma_16x16x128_fp8(af, bf[j]);
+                const float4 f = (MODE == 0 && j >= 2) ? f1 : f0;
+                acc[mt][j][0] += f.x * r[0];
+                acc[mt][j][1] += f.y * r[1];
+                acc[mt][j][2] += f.z * r[2];
+                acc[mt][j][3] += f.w * r[3];
+            }
+        }
+        wait_pending(pend_end);
+        __syncthreads();
+    }
+
+    if constexpr (MODE == 0) {
+        // ---- h = silu(g) * u, per-row amax over the 128 columns, e4m3 requantisation
+        uint8_t* out = smem;                                        // [BM][128] codes
+        float* sRed = reinterpret_cast<float*>(smem + BM * 128);    // [4][BM] row maxima
+        float h[MT][2][4];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                float m = 0.0f;
+#pragma unroll
+                for (int jj = 0; jj < 2; ++jj) {
+                    const float v = silu_fast(acc[mt][jj][i]) * acc[mt][jj + 2][i];
+                    h[mt][jj][i] = v;
+                    m = __builtin_fmaxf(m, __builtin_fabsf(v));
+                }
+#pragma unroll
+                for (int msk = 8; msk >= 1; msk >>= 1) m = __builtin_fmaxf(m, __shfl_xor(m, msk, 16));
+                if (rlane == 0) sRed[wn * BM + wm * MT * 16 + mt * 16 + 4 * kg + i] = m;
+            }
+        __syncthreads();
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int row = wm * MT * 16 + mt * 16 + 4 * kg + i;
+                const float amax = __builtin_fmaxf(__builtin_fmaxf(sRed[row], sRed[BM + row]),
+                                                   __builtin_fmaxf(sRed[2 * BM + row], sRed[3 * BM + row]));
+                const float sc = group_scale(amax);
+#pragma unroll
+                for (int jj = 0; jj < 2; ++jj)
+                    out[row * 128 + wn * 32 + jj * 16 + rlane] = (uint8_t)f32x2_to_e4m3(h[mt][jj][i] / sc, 0.0f);
+                if (wn == 0 && rlane == 0 && row < nrows) P.hs[(p0 + row) * NB128 + nb] = sc;
+            }
+        __syncthreads();
+        for (int c = tid; c < BM * 8; c += C::THREADS) {
+            const int row = c >> 3;
+            if (row < nrows)
+                *reinterpret_cast<uint4*>(P.hq + (p0 + row) * P.Ndim + n0 + (c & 7) * 16) =
+                    *reinterpret_cast<const uint4*>(out + row * 128 + (c & 7) * 16);
+        }
+    } else {
+        // ---- bf16 Y tile [BM][256] through LDS, coalesced 16-B stores of valid rows/columns
+        uint16_t* out = reinterpret_cast<uint16_t*>(smem);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int row = wm * MT * 16 + mt * 16 + 4 * kg + i;
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    out[row * kOutPitch + wn * 64 + j * 16 + rlane] = (uint16_t)f32_to_bf16(acc[mt][j][i]);
+            }
+        __syncthreads();
+        const int ncols = P.Ndim - n0 < 256 ? P.Ndim - n0 : 256;
+        for (int c = tid; c < BM * 32; c += C::THREADS) {
+            const int row = c >> 5, cc = (c & 31) * 8;
+            if (row < nrows && cc < ncols)
+                *reinterpret_cast<uint4*>(P.y + (p0 + row) * P.Ndim + n0 + cc) =
+                    *reinterpret_cast<const uint4*>(out + row * kOutPitch + cc);
+        }
+    }
+}
+
+template <int MODE, int MT>
+hipError_t launch_lds(const LdsGemmParams& P, int64_t max_tiles, hipStream_t stream) {
+    using C = Cfg<MODE, MT>;
+    const int64_t n_blocks = MODE == 0 ? P.Ndim / 128 : (P.Ndim + 255) / 256;
+    int64_t grid = max_tiles * n_blocks;
+    grid = (grid + kXcds - 1) / kXcds * kXcds;
+    if (grid <= 0) return hipSuccess;
+    if (grid > 0x7fffffff) return hipErrorInvalidValue;
+    static bool attr_set = false;  // raise the dynamic LDS limit once per instantiation
+    if (!attr_set) {
+        hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm_lds<MODE, MT>),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS);
+        if (err != hipSuccess) return err;
+        attr_set = true;
+    }
+    hipLaunchKernelGGL((k_gemm_lds<MODE, MT>), dim3((unsigned)grid), dim3(C::THREADS), C::LDS, stream, P);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_gate_up_lds(const GateUpArgs& a, int rows, hipStream_t stream) {
+    LdsGemmParams P{};
+    P.a = a.xq; P.as = a.xs; P.gather = a.sorted_slot; P.K_top = a.K; P.src_rows = a.N;
+    P.Kdim = a.d; P.Ndim = a.d_ff;
+    P.w0 = a.wg; P.s0 = a.sg; P.w1 = a.wu; P.s1 = a.su;
+    P.tiles = a.tiles; P.num_tiles = a.num_tiles;
+    P.hq = a.hq; P.hs = a.hs;
+    switch (rows) {
+        case 128: return launch_lds<0, 4>(P, a.max_tiles, stream);
+        case 192: return launch_lds<0, 6>(P, a.max_tiles, stream);
+        default: return launch_lds<0, 8>(P, a.max_tiles, stream);
+    }
+}
+
+hipError_t launch_down_lds(const DownArgs& a, int rows, hipStream_t stream) {
+    LdsGemmParams P{};
+    P.a = a.hq; P.as = a.hs; P.gather = nullptr; P.K_top = 1; P.src_rows = a.rows;
+    P.Kdim = a.d_ff; P.Ndim = a.d;
+    P.w0 = a.wd; P.s0 = a.sd;
+    P.tiles = a.tiles; P.num_tiles = a.num_tiles;
+    P.y = a.y;
+    switch (rows) {
+        case 128: return launch_lds<1, 4>(P, a.max_tiles, stream);
+        case 192: return launch_lds<1, 6>(P, a.max_tiles, stream);
+        default: return launch_lds<1, 8>(P, a.max_tiles, stream);
+    }
+}
+
+}  // namespace moe

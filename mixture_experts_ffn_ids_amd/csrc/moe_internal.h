@@ -34,6 +34,12 @@ __device__ __forceinline__ uint32_t f32x2_to_e4m3(float a, float b) {
     return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false) & 0xffffu;
 }
 
+// silu(z) = z * sigmoid(z) with the hardware exponential and reciprocal (a few ulp; the
+// product is requantised to 3 mantissa bits right after).
+__device__ __forceinline__ float silu_fast(float z) {
+    return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z));
+}
+
 // Per-group scale from the group's largest magnitude: amax/448, or 1 for a zero group.
 __device__ __forceinline__ float group_scale(float amax) {
     return amax > 0.0f ? amax / kE4m3Max : 1.0f;
@@ -59,12 +65,15 @@ hipError_t launch_dispatch(const int32_t* ids, int64_t N, int K, int E, int32_t*
                            int32_t* chunk_counts, int32_t* err_flag, bool checked,
                            hipStream_t stream);
 
-// Tile list: one entry per (expert, block of up to BM sorted rows).
+// Tile list: one entry per (expert, block of up to BM sorted rows), experts in order.
+// first/count: index of the expert's first tile and its number of tiles.
 struct Tile {
     int32_t expert;
     int32_t row_begin;
     int32_t row_end;
-    int32_t pad;
+    int32_t first;
+    int32_t count;
+    int32_t pad[3];
 };
 
 int64_t max_tiles(int64_t rows, int E, int BM);
@@ -72,7 +81,7 @@ int64_t max_tiles(int64_t rows, int E, int BM);
 hipError_t launch_build_tiles(const int32_t* offsets, int E, int64_t rows, int BM, int64_t max_tiles,
                               Tile* tiles, int32_t* num_tiles, hipStream_t stream);
 
-enum class TileShape { Small = 0, Medium = 1, Large = 2 };
+enum class TileShape { Rows16 = 0, Rows128 = 1, Rows192 = 2, Rows256 = 3 };
 int tile_rows(TileShape shape);   // BM of the gate|up and down kernels for this shape
 
 struct GateUpArgs {
@@ -101,6 +110,11 @@ struct DownArgs {
 
 hipError_t launch_gate_up(const GateUpArgs& a, TileShape shape, hipStream_t stream);
 hipError_t launch_down(const DownArgs& a, TileShape shape, hipStream_t stream);
+
+// LDS-staged kernels for tiles of 128, 192 or 256 rows (gemm_lds.hip)
+hipError_t launch_gate_up_lds(const GateUpArgs& a, int rows, hipStream_t stream);
+hipError_t launch_down_lds(const DownArgs& a, int rows, hipStream_t stream);
+
 
 hipError_t launch_combine(const uint16_t* y, const int32_t* slot_pos, const float* w,
                           const uint16_t* shared, int64_t N, int K, int d, uint16_t* out,

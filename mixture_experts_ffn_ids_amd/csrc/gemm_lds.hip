@@ -15,19 +15,25 @@
 // requantisation group is complete), for down 256 output columns. Each wave computes
 // 16 MT rows x 4 weight-row subtiles of 16 (64 columns): MT x 4 MFMA tiles.
 //
+// The weights are the MFMA's first operand and the token rows its second, so a lane's
+// four results belong to one token row (lane & 15) and four consecutive weight rows. The
+// activation scale is then one number per lane and row subtile, and the weight block scale
+// one number per wave: the per-block factor costs a broadcast read and a multiply instead
+// of a table lookup per result.
+//
 // Data movement per 128-wide K block, all by global_load_lds (lane L of a wave writes its
 // 16 bytes at LDS base + 16 L; no registers involved):
-//   * weights (256 x 128 B) and activations (BM x 128 B, gathered token rows for gate|up)
-//     into rings of 3 stages for 128-row tiles and 2 for larger ones (LDS capacity), so one
-//     or two blocks are in flight while one is multiplied;
-//   * row scales one block earlier than their rows, so that the thread owning a row can
-//     turn them into the products with this workgroup's weight block scales (the factors
-//     the MFMA loop applies) one block ahead, without an extra barrier.
+//   * weights (256 x 128 B) into a ring of 3 stages (2 for 256-row tiles, where LDS runs
+//     out), so that two weight blocks are in flight from HBM while one is multiplied;
+//   * activations (BM x 128 B, gathered token rows for gate|up) and their row scales into
+//     a ring of 3 stages for 128-row tiles and 2 otherwise (they come mostly from L2: the
+//     16 n-blocks of a tile run together on one XCD).
 // Rows are 128 B with 16-B chunks XOR-swizzled so that fragment reads are free of bank
-// conflicts. Rows past the end of the tile copy a valid row (the tile's first row, or the
-// last weight row); they are computed but never stored. The copies are written as inline
-// assembly so that the compiler does not wait for them at every LDS read; completion is
-// awaited explicitly (s_waitcnt vmcnt) before the barrier that publishes a block.
+// conflicts. Row scales are stored so that the MT scales one lane needs are adjacent.
+// Rows past the end of the tile copy a valid row (the tile's first row, or the last weight
+// row); they are computed but never stored. The copies are written as inline assembly so
+// that the compiler does not wait for them at every LDS read; completion is awaited
+// explicitly (s_waitcnt vmcnt) before the barrier that publishes a block.
 //
 // Scheduling: workgroups are dispatched round-robin over the 8 XCDs. The workgroup id is
 // remapped so that each XCD gets a contiguous range of (expert, n-block, row tile) items:
@@ -44,6 +50,7 @@ namespace {
 
 constexpr int kXcds = 8;
 constexpr int kOutPitch = 256 + 8;  // bf16 elements per row of the staged down-GEMM output
+constexpr int kCodePitch = 144;     // bytes per row of the staged gate|up codes
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
@@ -55,22 +62,23 @@ struct Cfg {
     static constexpr int BR = 256;                // weight rows per workgroup
     static constexpr int A_BYTES = BM * 128;      // one activation stage
     static constexpr int B_BYTES = BR * 128;      // one weight stage
-    // stages of the activation and weight rings: both three deep where LDS allows (128-row
-    // tiles); otherwise two (measured faster at 192 rows than a three-deep weight ring)
-    static constexpr int NA = BM <= 128 ? 3 : 2;
-    static constexpr int NBS = BM <= 128 ? 3 : 2;
+    static constexpr int NA = BM <= 128 ? 3 : 2;  // activation stages
+    static constexpr int NBS = BM <= 192 ? 3 : 2; // weight stages
     static constexpr int A_Q = BM / 64;           // 1-KB wave copies of A per wave per K block
     static constexpr int B_Q = BR / 64;           // same for B
-    static constexpr int S_Q = BM / 64;           // 256-B copies of row scales (waves 0..S_Q-1)
+    static constexpr int S_L = BM / NW;           // row scales copied by each wave (one copy)
     static constexpr int STAGES = NA * A_BYTES + NBS * B_BYTES;
-    static constexpr int OUT_BYTES = MODE == 1 ? BM * kOutPitch * 2 : BM * 128 + 4 * BM * 4;
+    static constexpr int OUT_BYTES = MODE == 1 ? BM * kOutPitch * 2 : BM * kCodePitch + 4 * BM * 4;
     static constexpr int MAIN = STAGES > OUT_BYTES ? STAGES : OUT_BYTES;
     static constexpr int MAX_KB = 65536 / 128;    // K blocks at the largest supported K
-    // LDS: A stages | B stages (or the output tile) | row scales [3][BM] | factors [2][2][BM]
-    //      | source rows [BM] | weight block scales [2][MAX_KB]
-    static constexpr int LDS = MAIN + 3 * BM * 4 + 4 * BM * 4 + BM * 4 + 2 * MAX_KB * 4;
+    // LDS: A stages | B stages (or the output tile) | row scales [NA][BM] | source rows [BM]
+    //      | weight block scales [2][MAX_KB]
+    static constexpr int LDS = MAIN + NA * BM * 4 + BM * 4 + 2 * MAX_KB * 4;
     static_assert(A_Q * NW * 64 == BM * 8 && B_Q * NW * 64 == BR * 8, "copy split");
-    static_assert(S_Q <= NW && BM <= THREADS, "scale copies");
+    // copies a wave may leave in flight at the end of a steady-state iteration: those issued
+    // in it for blocks that are not needed next
+    static constexpr int PEND = NA == 3 ? A_Q + 1 + B_Q : (NBS == 3 ? B_Q : 0);
+    static_assert(S_L <= 64 && BM % NW == 0 && MT % 2 == 0, "scale copies");
     static_assert(LDS <= 160 * 1024, "LDS budget");
     static_assert(A_Q + B_Q + 1 <= 15, "pending copies fit the wait helper");
 };
@@ -107,17 +115,19 @@ __device__ __forceinline__ v8i lds_frag(const uint8_t* tile, int r, int kg) {
     return v;
 }
 
-// Global -> LDS copies (global_load_lds): lane L writes its 16 (or 4) bytes at
-// l + 16 L (or 4 L); l must be the same for the whole wave.
+// Global -> LDS copies (global_load_lds): lane L writes its 16 (or 4) bytes at LDS byte
+// address l + 16 L (or 4 L); l must be the same for the whole wave.
 __device__ __forceinline__ uint32_t lds_addr(const void* l) {
-    return __builtin_amdgcn_readfirstlane((uint32_t)(size_t)(lds_ptr_t)(l));
+    return (uint32_t)(size_t)(lds_ptr_t)(l);
 }
-__device__ __forceinline__ void copy16(const uint8_t* g, uint8_t* l) {
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_addr(l)), "v"(g)
+__device__ __forceinline__ void copy16(const uint8_t* g, uint32_t l) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(
+                     __builtin_amdgcn_readfirstlane(l)), "v"(g)
                  : "memory", "m0");
 }
-__device__ __forceinline__ void copy4(const float* g, float* l) {
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off" ::"s"(lds_addr(l)), "v"(g)
+__device__ __forceinline__ void copy4(const float* g, uint32_t l) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off" ::"s"(
+                     __builtin_amdgcn_readfirstlane(l)), "v"(g)
                  : "memory", "m0");
 }
 // wait until at most N of this wave's copies are still in flight (they complete in order)
@@ -147,19 +157,25 @@ __device__ __forceinline__ void wait_pending(int n) {
     }
 }
 
+// Row of the tile whose activation scale sits in slot `slot` of a row-scale stage: the MT
+// scales of row subtiles 0..MT-1 that lane t of row-wave wm needs are adjacent, at
+// wm * 16 MT + t * MT.
+template <int MT>
+__device__ __forceinline__ int scale_slot_row(int slot) {
+    const int wm = slot / (MT * 16), rem = slot % (MT * 16);
+    return wm * MT * 16 + (rem % MT) * 16 + rem / MT;
+}
 
 template <int MODE, int MT>
 __global__ __launch_bounds__(512) void k_gemm_lds(const LdsGemmParams P) {
     using C = Cfg<MODE, MT>;
-    constexpr int BM = C::BM, NBS = C::NBS;
+    constexpr int BM = C::BM, NA = C::NA, NBS = C::NBS;
 
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-    constexpr int NA = C::NA;
     uint8_t* const sA = smem;                                   // [NA][BM][128]
     uint8_t* const sB = smem + NA * C::A_BYTES;                 // [NBS][256][128]
-    float* const sSA = reinterpret_cast<float*>(smem + C::MAIN); // [3][BM] row scales
-    float* const sF = sSA + 3 * BM;                             // [2][2][BM] factors
-    int32_t* const sRow = reinterpret_cast<int32_t*>(sF + 4 * BM);  // [BM]
+    float* const sSA = reinterpret_cast<float*>(smem + C::MAIN); // [NA][BM] row scales
+    int32_t* const sRow = reinterpret_cast<int32_t*>(sSA + NA * BM);  // [BM]
     float* const sSw = reinterpret_cast<float*>(sRow + BM);     // [2][MAX_KB]
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -239,31 +255,28 @@ __global__ __launch_bounds__(512) void k_gemm_lds(const LdsGemmParams P) {
             bOff[i] = (uint32_t)col * (uint32_t)P.Kdim + lchunk * 16;
         }
     }
-    const uint32_t sOff = wave < C::S_Q ? (uint32_t)sRow[wave * 64 + lane] * (uint32_t)KB : 0u;
+    // lanes 0 .. S_L-1 of every wave copy the row scales of slots wave * S_L + lane (one copy
+    // per wave and block, so that every wave has the same number of copies in flight)
+    const bool s_lane = lane < C::S_L;
+    const uint32_t sOff =
+        s_lane ? (uint32_t)sRow[scale_slot_row<MT>(wave * C::S_L + lane)] * (uint32_t)KB : 0u;
 
+    // activations of K block kb with their row scales (LDS addresses as 32-bit offsets)
+    const uint32_t ldsA = lds_addr(sA) + wave * 1024, ldsB = lds_addr(sB) + wave * 1024;
+    const uint32_t ldsS = lds_addr(sSA) + wave * C::S_L * 4;
     auto issueA = [&](int kb) {
-        uint8_t* A = sA + (kb % NA) * C::A_BYTES;
+        const uint32_t A = ldsA + (kb % NA) * C::A_BYTES;
         const uint32_t ko = (uint32_t)kb * 128;
 #pragma unroll
         for (int i = 0; i < C::A_Q; ++i)
-            copy16(P.a + (size_t)aRow[i] * P.Kdim + lchunk * 16 + ko, A + (wave + i * C::NW) * 1024);
-    };
-    auto issueS = [&](int kb) {
-        if (wave < C::S_Q) copy4(P.as + sOff + kb, sSA + (kb % 3) * BM + wave * 64);
+            copy16(P.a + (size_t)aRow[i] * P.Kdim + lchunk * 16 + ko, A + i * C::NW * 1024);
+        if (s_lane) copy4(P.as + sOff + kb, ldsS + (kb % NA) * BM * 4);
     };
     auto issueB = [&](int kb) {
-        uint8_t* B = sB + (kb % NBS) * C::B_BYTES;
+        const uint32_t B = ldsB + (kb % NBS) * C::B_BYTES;
         const uint32_t ko = (uint32_t)kb * 128;
 #pragma unroll
-        for (int i = 0; i < C::B_Q; ++i) copy16(bBase[i] + bOff[i] + ko, B + (wave + i * C::NW) * 1024);
-    };
-    // factors of K block kb (its row scales have landed): F[kb & 1][which][row]
-    auto factors = [&](int kb) {
-        if (tid < BM) {
-            const float sa = sSA[(kb % 3) * BM + tid];
-            sF[((kb & 1) * 2 + 0) * BM + tid] = sa * sSw[kb];
-            sF[((kb & 1) * 2 + 1) * BM + tid] = sa * sSw[C::MAX_KB + kb];
-        }
+        for (int i = 0; i < C::B_Q; ++i) copy16(bBase[i] + bOff[i] + ko, B + i * C::NW * 1024);
     };
 
     // weight-row base (within the B tile) of this wave's 4 subtiles
@@ -278,129 +291,149 @@ __global__ __launch_bounds__(512) void k_gemm_lds(const LdsGemmParams P) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[mt][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-    // ---- pipeline. Block kb's activations are copied NA-1 iterations ahead, its weights
-    // NBS-1 ahead and its row scales NA ahead (one earlier than its rows, so their factors can
-    // be formed the iteration before the block is used). At the end of iteration kb, block
-    // kb+1 (and the scales of kb+2) must have landed; copies that may still be in flight then
-    // are issued last, so an in-order count of pending copies is an exact wait.
-    const int sq = wave < C::S_Q ? 1 : 0;   // this wave copies one 64-row slice of scales
-    // prologue: everything block 0 and 1's factors need, then the copies that may stay pending
-    issueB(0);
-    issueA(0);
-    issueS(0);
-    if (KB > 1) issueS(1);
-    int pend = 0;
-    if (NA == 3 && KB > 1) { issueA(1); pend += C::A_Q; }
-    if (NBS == 3 && KB > 1) { issueB(1); pend += C::B_Q; }
-    if (NA == 3 && KB > 2) { issueS(2); pend += sq; }
-    wait_pending(pend);
-    __syncthreads();
-    factors(0);
-    __syncthreads();
-
     const int rlane = lane & 15, kg = lane >> 4;
-    // gate|up: subtiles 0,1 gate and 2,3 up use factor tables 0 and 1; down: the wave's
-    // 64 columns lie in 128-column block wn >> 1
-    const int ftab = MODE == 0 ? 0 : (wn >> 1);
-    for (int kb = 0; kb < KB; ++kb) {
-        // refill the buffers read in iteration kb - 1 (the barrier below separates them);
-        // copies that must land by the end of this iteration first, those that may not, last
-        const bool iA = kb + NA - 1 < KB, iB = kb + NBS - 1 < KB, iS = kb + NA < KB;
-        int pend_end = 0;
-        if (NA == 2 && NBS == 2) {
-            if (iB) issueB(kb + 1);
-            if (iA) issueA(kb + 1);
-            if (iS) issueS(kb + 2);
-        } else if (NA == 2) {      // NBS == 3: only the weights may stay in flight
-            if (iA) issueA(kb + 1);
-            if (iS) issueS(kb + 2);
-            if (iB) { issueB(kb + 2); pend_end = C::B_Q; }
-        } else {                   // NA == NBS == 3: all of this iteration's copies may
-            if (iB) { issueB(kb + 2); pend_end += C::B_Q; }
-            if (iA) { issueA(kb + 2); pend_end += C::A_Q; }
-            if (iS) { issueS(kb + 3); pend_end += sq; }
-        }
-        if (kb + 1 < KB) factors(kb + 1);
+    // weight block scale table of the wave's columns: gate|up subtiles 0,1 gate (table 0),
+    // 2,3 up (table 1); down: the wave's 64 columns lie in 128-column block wn >> 1
+    const int wtab0 = MODE == 0 ? 0 : (wn >> 1);
+    const float* const sSw0 = sSw + wtab0 * C::MAX_KB;
+    const float* const sSw1 = sSw + (MODE == 0 ? 1 : wtab0) * C::MAX_KB;
+    const int sa_slot = wm * MT * 16 + rlane * MT;
 
+    // multiply K block kb (landed and published) into the accumulators
+    auto compute = [&](int kb) {
         const uint8_t* A = sA + (kb % NA) * C::A_BYTES;
         const uint8_t* B = sB + (kb % NBS) * C::B_BYTES;
-        const float* F = sF + (kb & 1) * 2 * BM;
+        const float* SA = sSA + (kb % NA) * BM + sa_slot;
+        const float w0 = sSw0[kb], w1 = sSw1[kb];
         v8i bf[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) bf[j] = lds_frag(B, bbase[j] + rlane, kg);
+        float sa[MT];
+#pragma unroll
+        for (int mt = 0; mt < MT; mt += 2) {
+            const float2 v = *reinterpret_cast<const float2*>(SA + mt);
+            sa[mt] = v.x;
+            sa[mt + 1] = v.y;
+        }
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
             const int rb = wm * MT * 16 + mt * 16;
             const v8i af = lds_frag(A, rb + rlane, kg);
-            const float4 f0 = *reinterpret_cast<const float4*>(F + ftab * BM + rb + 4 * kg);
-            const float4 f1 = MODE == 0 ? *reinterpret_cast<const float4*>(F + BM + rb + 4 * kg) : f0;
+            const float f0 = sa[mt] * w0;
+            const float f1 = MODE == 0 ? sa[mt] * w1 : f0;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const v4f r = mfma_16x16x128_fp8(af, bf[j]);
-                const float4 f = (MODE == 0 && j >= 2) ? f1 : f0;
-                acc[mt][j][0] += f.x * r[0];
-                acc[mt][j][1] += f.y * r[1];
-                acc[mt][j][2] += f.z * r[2];
-                acc[mt][j][3] += f.w * r[3];
+                const v4f r = mfma_16x16x128_fp8(bf[j], af);
+                const float f = (MODE == 0 && j >= 2) ? f1 : f0;
+                acc[mt][j][0] += f * r[0];
+                acc[mt][j][1] += f * r[1];
+                acc[mt][j][2] += f * r[2];
+                acc[mt][j][3] += f * r[3];
             }
         }
-        wait_pending(pend_end);
+    };
+
+    // ---- pipeline. Block kb's activations (with their row scales) are copied NA-1
+    // iterations ahead and its weights NBS-1 ahead. At the end of iteration kb, block kb+1
+    // must have landed; the copies that may still be in flight then are the ones issued last,
+    // so an in-order count of pending copies is an exact wait.
+    issueB(0);
+    issueA(0);
+    int pend = 0;
+    if (NA == 3 && KB > 1) { issueA(1); pend += C::A_Q + 1; }
+    if (NBS == 3 && KB > 1) { issueB(1); pend += C::B_Q; }
+    wait_pending(pend);
+    __syncthreads();
+
+    // steady state: every ring is refilled in every iteration, and the wait count is a
+    // constant (no branch between the matrix work and the wait, so it stays ahead of it)
+    constexpr int AHEAD = (NA > NBS ? NA : NBS) - 1;
+    int kb = 0;
+    for (; kb < KB - AHEAD; ++kb) {
+        // refill the buffers read in iteration kb - 1 (the barrier below separates them);
+        // copies that must land by the end of this iteration first, those that may not, last
+        if (NA == 2 && NBS == 2) {
+            issueB(kb + 1);
+            issueA(kb + 1);
+        } else if (NA == 2) {
+            issueA(kb + 1);
+            issueB(kb + 2);
+        } else {
+            issueB(kb + 2);
+            issueA(kb + 2);
+        }
+        compute(kb);
+        __builtin_amdgcn_sched_barrier(0);
+        wait_copies<C::PEND>();
+        __syncthreads();
+    }
+    // the last AHEAD blocks: what is left to copy, then drain
+    for (; kb < KB; ++kb) {
+        if (NA == 2 && NBS == 3 && kb + 1 < KB) issueA(kb + 1);
+        compute(kb);
+        __builtin_amdgcn_sched_barrier(0);
+        wait_copies<0>();
         __syncthreads();
     }
 
+    // acc[mt][j][i]: row rb + rlane of the tile (rb = wm MT 16 + 16 mt), weight row
+    // bbase[j] + 4 kg + i of the workgroup's 256
     if constexpr (MODE == 0) {
         // ---- h = silu(g) * u, per-row amax over the 128 columns, e4m3 requantisation
-        uint8_t* out = smem;                                        // [BM][128] codes
-        float* sRed = reinterpret_cast<float*>(smem + BM * 128);    // [4][BM] row maxima
+        uint8_t* out = smem;                                          // [BM][kCodePitch] codes
+        float* sRed = reinterpret_cast<float*>(smem + BM * kCodePitch); // [4][BM] row maxima
         float h[MT][2][4];
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
+        for (int mt = 0; mt < MT; ++mt) {
+            float m = 0.0f;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                float m = 0.0f;
+            for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
-                for (int jj = 0; jj < 2; ++jj) {
+                for (int i = 0; i < 4; ++i) {
                     const float v = silu_fast(acc[mt][jj][i]) * acc[mt][jj + 2][i];
                     h[mt][jj][i] = v;
                     m = __builtin_fmaxf(m, __builtin_fabsf(v));
                 }
-#pragma unroll
-                for (int msk = 8; msk >= 1; msk >>= 1) m = __builtin_fmaxf(m, __shfl_xor(m, msk, 16));
-                if (rlane == 0) sRed[wn * BM + wm * MT * 16 + mt * 16 + 4 * kg + i] = m;
-            }
+            m = __builtin_fmaxf(m, __shfl_xor(m, 16));
+            m = __builtin_fmaxf(m, __shfl_xor(m, 32));
+            if (kg == 0) sRed[wn * BM + wm * MT * 16 + mt * 16 + rlane] = m;
+        }
         __syncthreads();
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
+        for (int mt = 0; mt < MT; ++mt) {
+            const int row = wm * MT * 16 + mt * 16 + rlane;
+            const float amax = __builtin_fmaxf(__builtin_fmaxf(sRed[row], sRed[BM + row]),
+                                               __builtin_fmaxf(sRed[2 * BM + row], sRed[3 * BM + row]));
+            const float sc = group_scale(amax);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int row = wm * MT * 16 + mt * 16 + 4 * kg + i;
-                const float amax = __builtin_fmaxf(__builtin_fmaxf(sRed[row], sRed[BM + row]),
-                                                   __builtin_fmaxf(sRed[2 * BM + row], sRed[3 * BM + row]));
-                const float sc = group_scale(amax);
-#pragma unroll
-                for (int jj = 0; jj < 2; ++jj)
-                    out[row * 128 + wn * 32 + jj * 16 + rlane] = (uint8_t)f32x2_to_e4m3(h[mt][jj][i] / sc, 0.0f);
-                if (wn == 0 && rlane == 0 && row < nrows) P.hs[(p0 + row) * NB128 + nb] = sc;
+            for (int jj = 0; jj < 2; ++jj) {
+                const uint32_t lo = f32x2_to_e4m3(h[mt][jj][0] / sc, h[mt][jj][1] / sc);
+                const uint32_t hi = f32x2_to_e4m3(h[mt][jj][2] / sc, h[mt][jj][3] / sc);
+                *reinterpret_cast<uint32_t*>(out + row * kCodePitch + wn * 32 + jj * 16 + 4 * kg) = lo | (hi << 16);
             }
+            if (wn == 0 && kg == 0 && row < nrows) P.hs[(p0 + row) * NB128 + nb] = sc;
+        }
         __syncthreads();
         for (int c = tid; c < BM * 8; c += C::THREADS) {
             const int row = c >> 3;
             if (row < nrows)
                 *reinterpret_cast<uint4*>(P.hq + (p0 + row) * P.Ndim + n0 + (c & 7) * 16) =
-                    *reinterpret_cast<const uint4*>(out + row * 128 + (c & 7) * 16);
+                    *reinterpret_cast<const uint4*>(out + row * kCodePitch + (c & 7) * 16);
         }
     } else {
         // ---- bf16 Y tile [BM][256] through LDS, coalesced 16-B stores of valid rows/columns
         uint16_t* out = reinterpret_cast<uint16_t*>(smem);
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
+        for (int mt = 0; mt < MT; ++mt) {
+            const int row = wm * MT * 16 + mt * 16 + rlane;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int row = wm * MT * 16 + mt * 16 + 4 * kg + i;
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    out[row * kOutPitch + wn * 64 + j * 16 + rlane] = (uint16_t)f32_to_bf16(acc[mt][j][i]);
+            for (int j = 0; j < 4; ++j) {
+                uint2 v;
+                v.x = f32_to_bf16(acc[mt][j][0]) | (f32_to_bf16(acc[mt][j][1]) << 16);
+                v.y = f32_to_bf16(acc[mt][j][2]) | (f32_to_bf16(acc[mt][j][3]) << 16);
+                *reinterpret_cast<uint2*>(out + row * kOutPitch + wn * 64 + j * 16 + 4 * kg) = v;
             }
+        }
         __syncthreads();
         const int ncols = P.Ndim - n0 < 256 ? P.Ndim - n0 : 256;
         for (int c = tid; c < BM * 32; c += C::THREADS) {

@@ -22,7 +22,10 @@
 // of a table lookup per result.
 //
 // Data movement per 128-wide K block, all by global_load_lds (lane L of a wave writes its
-// 16 bytes at LDS base + 16 L; no registers involved):
+// 16 bytes at LDS base + 16 L; no registers involved). Waves 0-3 copy activations, waves
+// 4-7 weights: a wave's copies complete in issue order, so a wave that copied both would
+// wait for older weight copies (from HBM) before its newer activation copies (from L2)
+// counted as landed.
 //   * weights (256 x 128 B) into a ring of 3 stages (2 for 256-row tiles, where LDS runs
 //     out), so that two weight blocks are in flight from HBM while one is multiplied;
 //   * activations (BM x 128 B, gathered token rows for gate|up) and their row scales into
@@ -42,6 +45,8 @@
 //
 // Epilogue: results are staged through the (then idle) stage buffers and written with
 // coalesced 16-byte stores.
+#include <type_traits>
+
 #include "moe_internal.h"
 
 namespace moe {
@@ -64,23 +69,24 @@ struct Cfg {
     static constexpr int B_BYTES = BR * 128;      // one weight stage
     static constexpr int NA = BM <= 128 ? 3 : 2;  // activation stages
     static constexpr int NBS = BM <= 192 ? 3 : 2; // weight stages
-    static constexpr int A_Q = BM / 64;           // 1-KB wave copies of A per wave per K block
-    static constexpr int B_Q = BR / 64;           // same for B
-    static constexpr int S_L = BM / NW;           // row scales copied by each wave (one copy)
+    // waves 0..3 copy the activations and their row scales, waves 4..7 the weights, so that
+    // each wave's in-order copy counter tracks one ring only
+    static constexpr int ROLE_W = NW / 2;
+    static constexpr int A_Q = BM * 8 / (ROLE_W * 64);  // 1-KB copies of A per A-wave per block
+    static constexpr int B_Q = BR * 8 / (ROLE_W * 64);  // same for B per B-wave
+    static constexpr int S_L = BM / ROLE_W;       // row scales copied by each A-wave (one copy)
+    static constexpr int S_STAGE = ROLE_W * 64;   // floats per row-scale stage (64 per A-wave)
     static constexpr int STAGES = NA * A_BYTES + NBS * B_BYTES;
     static constexpr int OUT_BYTES = MODE == 1 ? BM * kOutPitch * 2 : BM * kCodePitch + 4 * BM * 4;
     static constexpr int MAIN = STAGES > OUT_BYTES ? STAGES : OUT_BYTES;
     static constexpr int MAX_KB = 65536 / 128;    // K blocks at the largest supported K
-    // LDS: A stages | B stages (or the output tile) | row scales [NA][BM] | source rows [BM]
-    //      | weight block scales [2][MAX_KB]
-    static constexpr int LDS = MAIN + NA * BM * 4 + BM * 4 + 2 * MAX_KB * 4;
-    static_assert(A_Q * NW * 64 == BM * 8 && B_Q * NW * 64 == BR * 8, "copy split");
-    // copies a wave may leave in flight at the end of a steady-state iteration: those issued
-    // in it for blocks that are not needed next
-    static constexpr int PEND = NA == 3 ? A_Q + 1 + B_Q : (NBS == 3 ? B_Q : 0);
-    static_assert(S_L <= 64 && BM % NW == 0 && MT % 2 == 0, "scale copies");
+    // LDS: A stages | B stages (or the output tile) | row scales [NA][S_STAGE] | source rows
+    //      [BM] | weight block scales [2][MAX_KB]
+    static constexpr int LDS = MAIN + NA * S_STAGE * 4 + BM * 4 + 2 * MAX_KB * 4;
+    static_assert(A_Q * ROLE_W * 64 == BM * 8 && B_Q * ROLE_W * 64 == BR * 8, "copy split");
+    static_assert(S_L <= 64 && BM % ROLE_W == 0 && MT % 2 == 0, "scale copies");
     static_assert(LDS <= 160 * 1024, "LDS budget");
-    static_assert(A_Q + B_Q + 1 <= 15, "pending copies fit the wait helper");
+    static_assert(A_Q + 1 <= 15 && B_Q <= 15, "pending copies fit the wait helper");
 };
 
 struct LdsGemmParams {
@@ -115,19 +121,27 @@ __device__ __forceinline__ v8i lds_frag(const uint8_t* tile, int r, int kg) {
     return v;
 }
 
-// Global -> LDS copies (global_load_lds): lane L writes its 16 (or 4) bytes at LDS byte
+// Global -> LDS copies (global_load_lds): lane L reads 16 (or 4) bytes at g + off (g the
+// same for the whole wave, off the lane's 32-bit byte offset) and writes them at LDS byte
 // address l + 16 L (or 4 L); l must be the same for the whole wave.
 __device__ __forceinline__ uint32_t lds_addr(const void* l) {
     return (uint32_t)(size_t)(lds_ptr_t)(l);
 }
-__device__ __forceinline__ void copy16(const uint8_t* g, uint32_t l) {
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(
-                     __builtin_amdgcn_readfirstlane(l)), "v"(g)
+// a wave-uniform pointer, made visibly uniform (scalar registers) for the copy's base operand
+__device__ __forceinline__ const void* uniform_ptr(const void* g) {
+    const uint64_t v = (uint64_t)g;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return (const void*)(((uint64_t)hi << 32) | lo);
+}
+__device__ __forceinline__ void copy16(const void* g, uint32_t off, uint32_t l) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(
+                     __builtin_amdgcn_readfirstlane(l)), "v"(off), "s"(uniform_ptr(g))
                  : "memory", "m0");
 }
-__device__ __forceinline__ void copy4(const float* g, uint32_t l) {
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off" ::"s"(
-                     __builtin_amdgcn_readfirstlane(l)), "v"(g)
+__device__ __forceinline__ void copy4(const void* g, uint32_t off, uint32_t l) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2" ::"s"(
+                     __builtin_amdgcn_readfirstlane(l)), "v"(off), "s"(uniform_ptr(g))
                  : "memory", "m0");
 }
 // wait until at most N of this wave's copies are still in flight (they complete in order)
@@ -174,8 +188,8 @@ __global__ __launch_bounds__(512) void k_gemm_lds(const LdsGemmParams P) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     uint8_t* const sA = smem;                                   // [NA][BM][128]
     uint8_t* const sB = smem + NA * C::A_BYTES;                 // [NBS][256][128]
-    float* const sSA = reinterpret_cast<float*>(smem + C::MAIN); // [NA][BM] row scales
-    int32_t* const sRow = reinterpret_cast<int32_t*>(sSA + NA * BM);  // [BM]
+    float* const sSA = reinterpret_cast<float*>(smem + C::MAIN); // [NA][S_STAGE] row scales
+    int32_t* const sRow = reinterpret_cast<int32_t*>(sSA + NA * C::S_STAGE);  // [BM]
     float* const sSw = reinterpret_cast<float*>(sRow + BM);     // [2][MAX_KB]
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -232,52 +246,23 @@ __global__ __launch_bounds__(512) void k_gemm_lds(const LdsGemmParams P) {
     __syncthreads();
 
     // ---- per-lane copy plan. Wave copy q fills rows 8q .. 8q+7 of a stage; lane L lands in
-    // row 8q + (L >> 3), slot L & 7, which holds logical chunk (L & 7) ^ (L >> 3) ^ (q & 1);
-    // all q of a wave (q = wave + i * 8) have the parity of the wave.
+    // row 8q + (L >> 3), slot L & 7, which holds logical chunk (L & 7) ^ (L >> 3) ^ (q & 1).
+    // A-wave w (0..3) makes copies q = w + 4i of the activations, B-wave w (4..7) copies
+    // q = w - 4 + 4i of the weights: all q of a wave have the parity of the wave.
+    const bool b_wave = wave >= C::ROLE_W;
+    const int rw = b_wave ? wave - C::ROLE_W : wave;
     const int lrow = lane >> 3;
     const int lchunk = (lane & 7) ^ lrow ^ (wave & 1);
-    uint32_t aRow[C::A_Q];
-#pragma unroll
-    for (int i = 0; i < C::A_Q; ++i) aRow[i] = (uint32_t)sRow[8 * (wave + i * C::NW) + lrow];
-    const uint8_t* bBase[C::B_Q];
-    uint32_t bOff[C::B_Q];
-#pragma unroll
-    for (int i = 0; i < C::B_Q; ++i) {
-        const int q = wave + i * C::NW;
-        const int r = 8 * q + lrow;
-        if (MODE == 0) {
-            bBase[i] = (q < 16 ? P.w0 : P.w1) + (int64_t)e * P.Ndim * P.Kdim;
-            bOff[i] = (uint32_t)(n0 + (r & 127)) * (uint32_t)P.Kdim + lchunk * 16;
-        } else {
-            bBase[i] = P.w0 + (int64_t)e * P.Ndim * P.Kdim;
-            int col = n0 + r;
-            col = col < P.Ndim ? col : P.Ndim - 1;
-            bOff[i] = (uint32_t)col * (uint32_t)P.Kdim + lchunk * 16;
-        }
-    }
-    // lanes 0 .. S_L-1 of every wave copy the row scales of slots wave * S_L + lane (one copy
-    // per wave and block, so that every wave has the same number of copies in flight)
-    const bool s_lane = lane < C::S_L;
+    // weight tensors of expert e; gate|up copies 0..3 are gate rows, 4..7 up rows
+    const uint8_t* const wBase0 = P.w0 + (int64_t)e * P.Ndim * P.Kdim;
+    const uint8_t* const wBase1 = (MODE == 0 ? P.w1 : P.w0) + (int64_t)e * P.Ndim * P.Kdim;
+    // row scales: lane L < S_L of A-wave rw copies the scale of slot rw * S_L + L into position
+    // rw * 64 + L of a stage; the other lanes copy a valid value into the padding (so the copy
+    // needs no branch)
     const uint32_t sOff =
-        s_lane ? (uint32_t)sRow[scale_slot_row<MT>(wave * C::S_L + lane)] * (uint32_t)KB : 0u;
-
-    // activations of K block kb with their row scales (LDS addresses as 32-bit offsets)
-    const uint32_t ldsA = lds_addr(sA) + wave * 1024, ldsB = lds_addr(sB) + wave * 1024;
-    const uint32_t ldsS = lds_addr(sSA) + wave * C::S_L * 4;
-    auto issueA = [&](int kb) {
-        const uint32_t A = ldsA + (kb % NA) * C::A_BYTES;
-        const uint32_t ko = (uint32_t)kb * 128;
-#pragma unroll
-        for (int i = 0; i < C::A_Q; ++i)
-            copy16(P.a + (size_t)aRow[i] * P.Kdim + lchunk * 16 + ko, A + i * C::NW * 1024);
-        if (s_lane) copy4(P.as + sOff + kb, ldsS + (kb % NA) * BM * 4);
-    };
-    auto issueB = [&](int kb) {
-        const uint32_t B = ldsB + (kb % NBS) * C::B_BYTES;
-        const uint32_t ko = (uint32_t)kb * 128;
-#pragma unroll
-        for (int i = 0; i < C::B_Q; ++i) copy16(bBase[i] + bOff[i] + ko, B + i * C::NW * 1024);
-    };
+        lane < C::S_L ? (uint32_t)sRow[scale_slot_row<MT>(rw * C::S_L + lane)] * (uint32_t)KB * 4u : 0u;
+    const uint32_t ldsA = lds_addr(sA) + rw * 1024, ldsB = lds_addr(sB) + rw * 1024;
+    const uint32_t ldsS = lds_addr(sSA) + rw * 256;
 
     // weight-row base (within the B tile) of this wave's 4 subtiles
     int bbase[4];
@@ -297,84 +282,147 @@ __global__ __launch_bounds__(512) void k_gemm_lds(const LdsGemmParams P) {
     const int wtab0 = MODE == 0 ? 0 : (wn >> 1);
     const float* const sSw0 = sSw + wtab0 * C::MAX_KB;
     const float* const sSw1 = sSw + (MODE == 0 ? 1 : wtab0) * C::MAX_KB;
+    // this lane's MT row scales: slots wm 16 MT + rlane MT + (0..MT-1), at padded positions
     const int sa_slot = wm * MT * 16 + rlane * MT;
+    const int sa_pos = (sa_slot / C::S_L) * 64 + sa_slot % C::S_L;
 
-    // multiply K block kb (landed and published) into the accumulators
-    auto compute = [&](int kb) {
-        const uint8_t* A = sA + (kb % NA) * C::A_BYTES;
-        const uint8_t* B = sB + (kb % NBS) * C::B_BYTES;
-        const float* SA = sSA + (kb % NA) * BM + sa_slot;
-        const float w0 = sSw0[kb], w1 = sSw1[kb];
-        v8i bf[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) bf[j] = lds_frag(B, bbase[j] + rlane, kg);
-        float sa[MT];
-#pragma unroll
-        for (int mt = 0; mt < MT; mt += 2) {
-            const float2 v = *reinterpret_cast<const float2*>(SA + mt);
-            sa[mt] = v.x;
-            sa[mt + 1] = v.y;
-        }
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-            const int rb = wm * MT * 16 + mt * 16;
-            const v8i af = lds_frag(A, rb + rlane, kg);
-            const float f0 = sa[mt] * w0;
-            const float f1 = MODE == 0 ? sa[mt] * w1 : f0;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const v4f r = mfma_16x16x128_fp8(bf[j], af);
-                const float f = (MODE == 0 && j >= 2) ? f1 : f0;
-                acc[mt][j][0] += f * r[0];
-                acc[mt][j][1] += f * r[1];
-                acc[mt][j][2] += f * r[2];
-                acc[mt][j][3] += f * r[3];
+    // The K loop, instantiated per copy role (BW: this wave copies weights) so that the
+    // copies it issues between the matrix ops are straight-line code.
+    auto run = [&](auto role) {
+        constexpr bool BW = decltype(role)::value;
+        constexpr int NQ = BW ? C::B_Q : C::A_Q + 1;  // copies per block (A: rows + scales)
+        constexpr int NR = BW ? NBS : NA;             // ring depth
+        constexpr bool KEEP_OFF = true;               // offsets held in registers
+        // byte offset of copy i in block 0: in the activations (A) or the weight tensor (B);
+        // the host keeps both below 2^32
+        auto off = [&](int i) -> uint32_t {
+            const int r = 8 * (rw + i * C::ROLE_W) + lrow;
+            if constexpr (!BW) {
+                return (uint32_t)sRow[r] * (uint32_t)P.Kdim + lchunk * 16;
+            } else {
+                int wrow = MODE == 0 ? n0 + (r & 127) : n0 + r;
+                wrow = wrow < P.Ndim ? wrow : P.Ndim - 1;
+                return (uint32_t)wrow * (uint32_t)P.Kdim + lchunk * 16;
             }
+        };
+        uint32_t cIdx[KEEP_OFF ? NQ : 1];
+        if constexpr (KEEP_OFF) {
+#pragma unroll
+            for (int i = 0; i < NQ; ++i) cIdx[i] = (!BW && i == C::A_Q) ? 0u : off(i);
         }
+        auto get_off = [&](int i) -> uint32_t {
+            if constexpr (KEEP_OFF) return cIdx[i]; else return off(i);
+        };
+        // issue copies [lo, hi) of block kb
+        auto issue = [&](int kb, int lo, int hi) {
+            const int ko = kb * 128;
+#pragma unroll
+            for (int i = 0; i < NQ; ++i) {
+                if (i < lo || i >= hi) continue;
+                if constexpr (!BW) {
+                    if (i < C::A_Q)
+                        copy16(P.a + ko, get_off(i), ldsA + (kb % NA) * C::A_BYTES + i * C::ROLE_W * 1024);
+                    else
+                        copy4(P.as + kb, sOff, ldsS + (kb % NA) * C::S_STAGE * 4);
+                } else {
+                    copy16((MODE == 0 && i >= C::B_Q / 2 ? wBase1 : wBase0) + ko, get_off(i),
+                           ldsB + (kb % NBS) * C::B_BYTES + i * C::ROLE_W * 1024);
+                }
+            }
+        };
+
+        // multiply K block kb (landed and published) into the accumulators; with ISSUE, also
+        // issue the copies of block `next`, spread over the row subtiles: a copy can stall its
+        // wave until the memory pipeline takes it, and spread out those stalls overlap the
+        // matrix work instead of preceding it
+        // Exception: with a 2-stage activation ring an A-wave issues its whole block first,
+        // for the most lead time (its copies must land by the end of this iteration).
+        constexpr int SLOTS = (BW || NA == 3) ? MT : 1;
+        auto compute = [&](int kb, auto issue_tag, int next) {
+            constexpr bool ISSUE = decltype(issue_tag)::value;
+            const uint8_t* A = sA + (kb % NA) * C::A_BYTES;
+            const uint8_t* B = sB + (kb % NBS) * C::B_BYTES;
+            const float* SA = sSA + (kb % NA) * C::S_STAGE + sa_pos;
+            const float w0 = sSw0[kb], w1 = sSw1[kb];
+            v8i bf[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) bf[j] = lds_frag(B, bbase[j] + rlane, kg);
+            float sa[MT];
+#pragma unroll
+            for (int mt = 0; mt < MT; mt += 2) {
+                const float2 v = *reinterpret_cast<const float2*>(SA + mt);
+                sa[mt] = v.x;
+                sa[mt + 1] = v.y;
+            }
+            // one row subtile at a time (a scheduling barrier after each keeps the compiler
+            // from gathering all of them, which would hold every fragment at once); the next
+            // subtile's activation fragment is read ahead
+            v8i af = lds_frag(A, wm * MT * 16 + rlane, kg);
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                v8i af_next;
+                if (mt + 1 < MT) af_next = lds_frag(A, wm * MT * 16 + (mt + 1) * 16 + rlane, kg);
+                if constexpr (ISSUE) {
+                    if (mt % (MT / SLOTS) == 0) {
+                        const int slot = mt / (MT / SLOTS);
+                        issue(next, slot * NQ / SLOTS, (slot + 1) * NQ / SLOTS);
+                    }
+                }
+                const float f0 = sa[mt] * w0;
+                const float f1 = MODE == 0 ? sa[mt] * w1 : f0;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const v4f r = mfma_16x16x128_fp8(bf[j], af);
+                    const float f = (MODE == 0 && j >= 2) ? f1 : f0;
+                    acc[mt][j][0] += f * r[0];
+                    acc[mt][j][1] += f * r[1];
+                    acc[mt][j][2] += f * r[2];
+                    acc[mt][j][3] += f * r[3];
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                if (mt + 1 < MT) af = af_next;
+            }
+        };
+
+        // ---- pipeline. Block kb's activations (with their row scales) are copied NA-1
+        // iterations ahead by the A-waves, its weights NBS-1 ahead by the B-waves. At the end
+        // of iteration kb, block kb+1 must have landed; what a wave may leave in flight then
+        // is the copies it issued last, so an in-order count of pending copies is an exact
+        // wait. Both roles pass the same number of barriers.
+        issue(0, 0, NQ);
+        if (NR == 3 && KB > 1) issue(1, 0, NQ);
+        wait_pending(NR == 3 && KB > 1 ? NQ : 0);
+        __syncthreads();
+
+        // steady state: every ring is refilled in every iteration and the wait count is a
+        // constant, with no branch between the matrix work and the wait
+        constexpr int AHEAD = (NA > NBS ? NA : NBS) - 1;
+        static_assert(AHEAD == 1 || AHEAD == 2, "ring depths of 2 or 3");
+        for (int kb = 0; kb < KB - AHEAD; ++kb) {
+            // refill the stage read in iteration kb - 1 (the barrier below separates them)
+            compute(kb, std::true_type{}, kb + NR - 1);
+            __builtin_amdgcn_sched_barrier(0);
+            wait_copies<NR == 3 ? NQ : 0>();
+            __syncthreads();
+        }
+        // the last AHEAD blocks (t = 0 .. AHEAD-1 is block KB - AHEAD + t, skipped when K is
+        // shorter): whether a role still has a block to copy is known at compile time
+        auto drain = [&](auto t_tag) {
+            constexpr int T = decltype(t_tag)::value;
+            const int kbt = KB - AHEAD + T;
+            if (kbt < 0) return;
+            compute(kbt, std::integral_constant<bool, (T + NR - 1 < AHEAD)>{}, kbt + NR - 1);
+            __builtin_amdgcn_sched_barrier(0);
+            wait_copies<0>();
+            __syncthreads();
+        };
+        drain(std::integral_constant<int, 0>{});
+        if constexpr (AHEAD > 1) drain(std::integral_constant<int, 1>{});
     };
-
-    // ---- pipeline. Block kb's activations (with their row scales) are copied NA-1
-    // iterations ahead and its weights NBS-1 ahead. At the end of iteration kb, block kb+1
-    // must have landed; the copies that may still be in flight then are the ones issued last,
-    // so an in-order count of pending copies is an exact wait.
-    issueB(0);
-    issueA(0);
-    int pend = 0;
-    if (NA == 3 && KB > 1) { issueA(1); pend += C::A_Q + 1; }
-    if (NBS == 3 && KB > 1) { issueB(1); pend += C::B_Q; }
-    wait_pending(pend);
-    __syncthreads();
-
-    // steady state: every ring is refilled in every iteration, and the wait count is a
-    // constant (no branch between the matrix work and the wait, so it stays ahead of it)
-    constexpr int AHEAD = (NA > NBS ? NA : NBS) - 1;
-    int kb = 0;
-    for (; kb < KB - AHEAD; ++kb) {
-        // refill the buffers read in iteration kb - 1 (the barrier below separates them);
-        // copies that must land by the end of this iteration first, those that may not, last
-        if (NA == 2 && NBS == 2) {
-            issueB(kb + 1);
-            issueA(kb + 1);
-        } else if (NA == 2) {
-            issueA(kb + 1);
-            issueB(kb + 2);
-        } else {
-            issueB(kb + 2);
-            issueA(kb + 2);
-        }
-        compute(kb);
-        __builtin_amdgcn_sched_barrier(0);
-        wait_copies<C::PEND>();
-        __syncthreads();
-    }
-    // the last AHEAD blocks: what is left to copy, then drain
-    for (; kb < KB; ++kb) {
-        if (NA == 2 && NBS == 3 && kb + 1 < KB) issueA(kb + 1);
-        compute(kb);
-        __builtin_amdgcn_sched_barrier(0);
-        wait_copies<0>();
-        __syncthreads();
-    }
+    if (b_wave)
+        run(std::true_type{});
+    else
+        run(std::false_type{});
 
     // acc[mt][j][i]: row rb + rlane of the tile (rb = wm MT 16 + 16 mt), weight row
     // bbase[j] + 4 kg + i of the workgroup's 256

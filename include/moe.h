@@ -71,7 +71,8 @@ typedef enum {
 #define MOE_FLAG_CHECKED 1u
 /* moe_grouped_swiglu: force the GEMM tile height (sorted rows of one expert per
  * workgroup) instead of choosing it from the expected rows per expert,
- * N*K / min(E, N*K). Results do not depend on it, bit for bit. */
+ * N*K / min(E, N*K). Results do not depend on it, bit for bit. Batches with
+ * N*d or N*K*d_ff at or above 2^32 bytes always use 16-row tiles. */
 #define MOE_FLAG_TILE_16 (1u << 4)
 #define MOE_FLAG_TILE_128 (2u << 4)
 #define MOE_FLAG_TILE_192 (3u << 4)

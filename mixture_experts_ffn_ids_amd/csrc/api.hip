@@ -128,7 +128,16 @@ SwigluWs swiglu_layout(int64_t N, int32_t K, int32_t E, int32_t d, int32_t d_ff)
 
 bool dim_ok(int32_t v) { return v > 0 && v % kGroup == 0 && v <= MOE_MAX_DIM; }
 
-TileShape choose_shape(int64_t rows, int32_t E, uint32_t flags) {
+// The many-row kernels address activations with 32-bit byte offsets from a per-block base:
+// token rows x d (gate|up) and sorted rows x d_ff (down) must stay below 2^32 bytes.
+// Larger batches use the 16-row kernel, which addresses with 64 bits.
+bool fits_32bit_offsets(int64_t N, int64_t rows, int32_t d, int32_t d_ff) {
+    const int64_t lim = (int64_t)1 << 32;
+    return N * (int64_t)d < lim && rows * (int64_t)d_ff < lim;
+}
+
+TileShape choose_shape(int64_t N, int64_t rows, int32_t E, int32_t d, int32_t d_ff, uint32_t flags) {
+    if (!fits_32bit_offsets(N, rows, d, d_ff)) return TileShape::Rows16;
     switch (flags & MOE_FLAG_TILE_MASK) {
         case MOE_FLAG_TILE_16: return TileShape::Rows16;
         case MOE_FLAG_TILE_128: return TileShape::Rows128;
@@ -239,7 +248,7 @@ moe_status moe_grouped_swiglu(const uint16_t* x, int64_t N, int32_t K, int32_t E
     Tile* tiles = (Tile*)(ws + L.tiles);
     int32_t* ntiles = (int32_t*)(ws + L.ntiles);
     const int64_t rows = N * K;
-    const TileShape shape = choose_shape(rows, E, flags);
+    const TileShape shape = choose_shape(N, rows, E, d, d_ff, flags);
     const int BM = tile_rows(shape);
     const int64_t cap = max_tiles(rows, E, BM);
 

@@ -51,10 +51,11 @@ def parse():
     return ap.parse_args()
 
 
-def gemm_source_sha256() -> str:
+def source_sha256(names) -> str:
+    """sha256 over the named kernel sources (files under the package's csrc/, in order)."""
     import hashlib
     h = hashlib.sha256()
-    for name in ("gemm.hip", "gemm_lds.hip", "moe_internal.h"):
+    for name in names:
         with open(os.path.join(ROOT, "mixture_experts_ffn_ids_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
@@ -63,7 +64,8 @@ def gemm_source_sha256() -> str:
 def stored_traffic(workload: str):
     """HBM bytes per gate|up launch from the committed rocprofv3 counter summary of this
     workload (FETCH_SIZE and WRITE_SIZE, scaled by the copy calibration), or None when
-    there is none or the kernel source has changed since the counters were taken."""
+    there is none or the kernel's sources (listed in the record) have changed since the
+    counters were taken."""
     path = os.path.join(ROOT, "profiles", f"gate_up_{workload}.md")
     if not os.path.exists(path):
         return None
@@ -72,7 +74,9 @@ def stored_traffic(workload: str):
         for line in f:
             if line.startswith("traffic-record:"):
                 rec = dict(kv.split("=", 1) for kv in line.split()[1:])
-    if not rec or rec.get("source_sha256") != gemm_source_sha256():
+    if not rec or "sources" not in rec:
+        return None
+    if rec.get("source_sha256") != source_sha256(rec["sources"].split(",")):
         return None
     kib = float(rec["fetch_kib"]) * float(rec["fetch_scale"]) + float(rec["write_kib"]) * float(rec["write_scale"])
     return int(kib * 1024)

@@ -254,12 +254,16 @@ __global__ __launch_bounds__(WM* WN * 64) void k_grouped_gemm(const GemmParams P
 #pragma unroll
                 for (int w = 0; w < WN; ++w) amax = __builtin_fmaxf(amax, sRed[w][row]);
                 const float sc = group_scale(amax);
+                float q[NT];
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt) q[nt] = h[mt][nt][i];
+                scale_group(q, sc);
                 if (row < nrows) {
                     const int64_t p = p0 + row;
 #pragma unroll
                     for (int nt = 0; nt < NT; ++nt) {
                         const int col = wcol0 + nt * 16 + (lane & 15);
-                        P.hq[p * dff + col] = (uint8_t)f32x2_to_e4m3(h[mt][nt][i] / sc, 0.0f);
+                        P.hq[p * dff + col] = (uint8_t)f32x2_to_e4m3(q[nt], 0.0f);
                     }
                     if (wn == 0 && (lane & 15) == 0) P.hs[p * (dff / 128) + n0 / 128] = sc;
                 }

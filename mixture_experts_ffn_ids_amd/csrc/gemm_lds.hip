@@ -453,10 +453,14 @@ __global__ __launch_bounds__(512) void k_gemm_lds(const LdsGemmParams P) {
             const float amax = __builtin_fmaxf(__builtin_fmaxf(sRed[row], sRed[BM + row]),
                                                __builtin_fmaxf(sRed[2 * BM + row], sRed[3 * BM + row]));
             const float sc = group_scale(amax);
+            float q[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) q[k] = h[mt][k >> 2][k & 3];
+            scale_group(q, sc);
 #pragma unroll
             for (int jj = 0; jj < 2; ++jj) {
-                const uint32_t lo = f32x2_to_e4m3(h[mt][jj][0] / sc, h[mt][jj][1] / sc);
-                const uint32_t hi = f32x2_to_e4m3(h[mt][jj][2] / sc, h[mt][jj][3] / sc);
+                const uint32_t lo = f32x2_to_e4m3(q[4 * jj], q[4 * jj + 1]);
+                const uint32_t hi = f32x2_to_e4m3(q[4 * jj + 2], q[4 * jj + 3]);
                 *reinterpret_cast<uint32_t*>(out + row * kCodePitch + wn * 32 + jj * 16 + 4 * kg) = lo | (hi << 16);
             }
             if (wn == 0 && kg == 0 && row < nrows) P.hs[(p0 + row) * NB128 + nb] = sc;

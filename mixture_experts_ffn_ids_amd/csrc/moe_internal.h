@@ -18,12 +18,9 @@ __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
     return __uint_as_float(bits16 << 16);
 }
 
-// float -> bfloat16 bits, nearest-even (finite inputs; NaN maps to a quiet NaN).
+// float -> bfloat16 bits, nearest-even: the hardware conversion (v_cvt_pk_bf16_f32).
 __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return u >> 16;
+    return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)f);
 }
 
 // Two floats -> two OCP e4m3 codes (nearest-even) in the low 16 bits; inputs are
@@ -43,6 +40,23 @@ __device__ __forceinline__ float silu_fast(float z) {
 // Per-group scale from the group's largest magnitude: amax/448, or 1 for a zero group.
 __device__ __forceinline__ float group_scale(float amax) {
     return amax > 0.0f ? amax / kE4m3Max : 1.0f;
+}
+
+// The values to encode, v / s, for the requantisation of h inside the GEMM epilogues: v times
+// the correctly rounded reciprocal of s (one division per group instead of one per value).
+// The product can differ from the quotient by an ulp, which moves an e4m3 code only when the
+// quotient lies within an ulp of a rounding midpoint. A subnormal s (reciprocal out of
+// range) takes the division; the branch is skipped unless some lane needs it.
+template <int NV>
+__device__ __forceinline__ void scale_group(float (&v)[NV], float s) {
+    if (s < 0x1p-126f) {
+#pragma unroll
+        for (int k = 0; k < NV; ++k) v[k] = v[k] / s;
+    } else {
+        const float inv = 1.0f / s;
+#pragma unroll
+        for (int k = 0; k < NV; ++k) v[k] = v[k] * inv;
+    }
 }
 
 // 16x16x128 FP8 x FP8 -> FP32 matrix core op with unit block scales (E8M0 127 = 2^0).

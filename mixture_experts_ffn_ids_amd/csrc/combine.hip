@@ -5,8 +5,8 @@
 // workgroup owns whole tokens and writes every output element exactly once, so
 // no atomics are needed and the result is deterministic.
 //
-// Memory-bound: a lane moves 8 bf16 (16 B) per row per step; the K source rows of
-// a token are 14 KB contiguous runs at K2 shapes.
+// Memory-bound: a lane moves 8 bf16 (16 B) per source row per chunk; the K source rows
+// of a token are 14 KB contiguous runs at K2 shapes.
 #include "moe_internal.h"
 
 namespace moe {
@@ -18,51 +18,88 @@ __device__ __forceinline__ void unpack8(const uint4 r, float (&f)[8]) {
     f[6] = bf16_to_f32(r.w & 0xffffu); f[7] = bf16_to_f32(r.w >> 16);
 }
 
+// One wave per (token, 1024-column slice); lane L owns 16-B chunks L and L + 64 of the
+// slice. The token's K source rows and weights are read once (lanes < K) and broadcast by
+// lane reads; for each batch of up to 8 choices every load of both chunks is issued before
+// any is accumulated, so a lane keeps up to 16 loads in flight.
+constexpr int kSliceChunks = 128;  // 16-B chunks (8 bf16) per wave slice
+
 __global__ __launch_bounds__(256) void k_combine(const uint16_t* __restrict__ y, const int32_t* __restrict__ slot_pos,
                                                  const float* __restrict__ w, const uint16_t* __restrict__ shared,
                                                  int64_t N, int K, int d, uint16_t* __restrict__ out) {
-    __shared__ int64_t sPos[kMaxTopK];
-    __shared__ float sW[kMaxTopK];
+    const int lane = threadIdx.x & 63;
+    const int chunks = d / 8;
+    const int slices = (chunks + kSliceChunks - 1) / kSliceChunks;
+    const int64_t wv = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int64_t n = wv / slices;
+    if (n >= N) return;  // uniform over the wave
+    const int c0 = (int)(wv % slices) * kSliceChunks + lane;
     const int64_t NK = N * K;
-    for (int64_t n = blockIdx.x; n < N; n += gridDim.x) {
-        __syncthreads();
-        if (threadIdx.x < K) {
-            const int32_t p = slot_pos[n * K + threadIdx.x];
-            sPos[threadIdx.x] = (p >= 0 && p < NK) ? (int64_t)p : -1;
-            sW[threadIdx.x] = w[n * K + threadIdx.x];
-        }
-        __syncthreads();
-        for (int c = threadIdx.x * 8; c < d; c += blockDim.x * 8) {
-            float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-            for (int k = 0; k < K; ++k) {
-                const int64_t p = sPos[k];
-                if (p < 0) continue;
-                float f[8];
-                unpack8(*reinterpret_cast<const uint4*>(y + p * d + c), f);
-                const float wk = sW[k];
+    int32_t my_p = -1;
+    float my_w = 0.0f;
+    if (lane < K) {
+        const int32_t p = slot_pos[n * K + lane];
+        my_p = (p >= 0 && p < NK) ? p : -1;
+        my_w = w[n * K + lane];
+    }
+    const bool v0 = c0 < chunks, v1 = c0 + 64 < chunks;
+    float acc[2][8];
 #pragma unroll
-                for (int i = 0; i < 8; ++i) acc[i] += wk * f[i];
-            }
-            if (shared) {
-                float f[8];
-                unpack8(*reinterpret_cast<const uint4*>(shared + n * d + c), f);
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
-                for (int i = 0; i < 8; ++i) acc[i] += f[i];
-            }
-            uint4 o;
-            o.x = f32_to_bf16(acc[0]) | (f32_to_bf16(acc[1]) << 16);
-            o.y = f32_to_bf16(acc[2]) | (f32_to_bf16(acc[3]) << 16);
-            o.z = f32_to_bf16(acc[4]) | (f32_to_bf16(acc[5]) << 16);
-            o.w = f32_to_bf16(acc[6]) | (f32_to_bf16(acc[7]) << 16);
-            *reinterpret_cast<uint4*>(out + n * d + c) = o;
+        for (int i = 0; i < 8; ++i) acc[j][i] = 0.0f;
+    for (int k0 = 0; k0 < K; k0 += 8) {
+        uint4 r[8][2];
+        int32_t pk[8];
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk) {
+            const int k = k0 + kk < K ? k0 + kk : K - 1;
+            pk[kk] = __shfl(my_p, k);
+            const bool ok = k0 + kk < K && pk[kk] >= 0;
+            const uint4* src = reinterpret_cast<const uint4*>(y + (int64_t)(ok ? pk[kk] : 0) * d) + c0;
+            r[kk][0] = (ok && v0) ? src[0] : make_uint4(0, 0, 0, 0);
+            r[kk][1] = (ok && v1) ? src[64] : make_uint4(0, 0, 0, 0);
         }
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk) {
+            const int k = k0 + kk < K ? k0 + kk : K - 1;
+            const float wk = __shfl(my_w, k);
+            if (k0 + kk < K && pk[kk] >= 0) {
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    float f[8];
+                    unpack8(r[kk][j], f);
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) acc[j][i] += wk * f[i];
+                }
+            }
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int c = c0 + 64 * j;
+        if (c >= chunks) continue;
+        if (shared) {
+            float f[8];
+            unpack8(*(reinterpret_cast<const uint4*>(shared + n * d) + c), f);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) acc[j][i] += f[i];
+        }
+        uint4 o;
+        o.x = f32_to_bf16(acc[j][0]) | (f32_to_bf16(acc[j][1]) << 16);
+        o.y = f32_to_bf16(acc[j][2]) | (f32_to_bf16(acc[j][3]) << 16);
+        o.z = f32_to_bf16(acc[j][4]) | (f32_to_bf16(acc[j][5]) << 16);
+        o.w = f32_to_bf16(acc[j][6]) | (f32_to_bf16(acc[j][7]) << 16);
+        *(reinterpret_cast<uint4*>(out + n * d) + c) = o;
     }
 }
 
 hipError_t launch_combine(const uint16_t* y, const int32_t* slot_pos, const float* w, const uint16_t* shared,
                           int64_t N, int K, int d, uint16_t* out, hipStream_t stream) {
     if (N == 0) return hipSuccess;
-    const int64_t blocks = N < 65536 ? N : 65536;
+    const int64_t slices = (d / 8 + kSliceChunks - 1) / kSliceChunks;
+    const int64_t blocks = (N * slices + 3) / 4;
+    if (blocks > 0x7fffffff) return hipErrorInvalidValue;
     hipLaunchKernelGGL(k_combine, dim3((unsigned)blocks), dim3(256), 0, stream, y, slot_pos, w, shared, N, K, d, out);
     return hipGetLastError();
 }

@@ -3,14 +3,15 @@
 // the scatter-of-ones column sum, the argsort of the flat ids and the running
 // start/end index of each expert's slice).
 //
-// Integer-only and deterministic. Three launches:
+// Integer-only and deterministic. Four launches:
 //   1. k_hist:    slots are cut into chunks of 256; each workgroup counts its
 //                 chunk per expert in LDS (integer LDS atomics -- the counts do not
-//                 depend on their order) and writes chunk_counts[chunk][E].
-//   2. k_scan:    one workgroup turns each expert's column of chunk counts into an
-//                 exclusive prefix (the chunk's base inside the expert's slice),
-//                 writes counts[E] and the exclusive scan offsets[E+1].
-//   3. k_permute: each slot's position is offsets[e] + chunk base + its rank among
+//                 depend on their order) and writes chunk_counts[E][chunk].
+//   2. k_colscan: one wave per expert turns its row of chunk counts into an exclusive
+//                 prefix (the chunk's base inside the expert's slice) and writes
+//                 counts[e].
+//   3. k_offsets: one workgroup writes the exclusive scan offsets[E+1] of the counts.
+//   4. k_permute: each slot's position is offsets[e] + chunk base + its rank among
 //                 the earlier slots of the same expert in its chunk, so the order
 //                 within an expert is ascending slot index (a stable sort).
 // Also builds the GEMM tile lists (k_tiles) from offsets.
@@ -19,7 +20,8 @@
 namespace moe {
 
 __global__ __launch_bounds__(kDispatchChunk) void k_hist(const int32_t* __restrict__ ids, int64_t NK,
-                                                         int K, int E, int32_t* __restrict__ chunk_counts,
+                                                         int K, int E, int nchunks,
+                                                         int32_t* __restrict__ chunk_counts,
                                                          int32_t* __restrict__ err, int checked) {
     extern __shared__ int32_t cnt[];  // [E]
     for (int e = threadIdx.x; e < E; e += blockDim.x) cnt[e] = 0;
@@ -38,8 +40,7 @@ __global__ __launch_bounds__(kDispatchChunk) void k_hist(const int32_t* __restri
         }
     }
     __syncthreads();
-    int32_t* out = chunk_counts + (int64_t)blockIdx.x * E;
-    for (int e = threadIdx.x; e < E; e += blockDim.x) out[e] = cnt[e];
+    for (int e = threadIdx.x; e < E; e += blockDim.x) chunk_counts[(int64_t)e * nchunks + blockIdx.x] = cnt[e];
 }
 
 // Block-wide exclusive scan of one value per thread (up to 1024 threads = 16 waves).
@@ -66,38 +67,54 @@ __device__ T block_exclusive_scan(T v, T* total) {
     return base + incl - v;
 }
 
-__global__ __launch_bounds__(1024) void k_scan(int32_t* __restrict__ chunk_counts, int nchunks, int E,
-                                               int32_t* __restrict__ counts, int32_t* __restrict__ offsets) {
-    extern __shared__ int32_t tot[];  // [E]
-    // column scan over chunks, one expert per thread (strided)
-    for (int e = threadIdx.x; e < E; e += blockDim.x) {
-        int32_t run = 0;
-        for (int c = 0; c < nchunks; ++c) {
-            int32_t* p = chunk_counts + (int64_t)c * E + e;
-            const int32_t v = *p;
-            *p = run;
-            run += v;
-        }
-        tot[e] = run;
-        counts[e] = run;
+// Per expert (one wave each, four per workgroup): exclusive prefix of its chunk counts, in
+// place, and its total. Lane L sums chunks [L per, (L+1) per), the lane sums are scanned
+// across the wave, and each lane rewrites its chunks as running bases.
+__global__ __launch_bounds__(256) void k_colscan(int32_t* __restrict__ chunk_counts, int nchunks, int E,
+                                                 int32_t* __restrict__ counts) {
+    const int lane = threadIdx.x & 63;
+    const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (e >= E) return;  // uniform over the wave
+    int32_t* row = chunk_counts + (int64_t)e * nchunks;
+    const int per = (nchunks + 63) / 64;
+    const int c0 = lane * per;
+    const int c1 = c0 + per < nchunks ? c0 + per : nchunks;
+    int32_t local = 0;
+    for (int c = c0; c < c1; ++c) local += row[c];
+    int32_t incl = local;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int32_t t = __shfl_up(incl, off, 64);
+        if (lane >= off) incl += t;
     }
-    __syncthreads();
-    // exclusive scan over experts: each thread owns a contiguous range
+    int32_t run = incl - local;
+    for (int c = c0; c < c1; ++c) {
+        const int32_t v = row[c];
+        row[c] = run;
+        run += v;
+    }
+    if (lane == 63) counts[e] = incl;
+}
+
+// offsets[E+1]: exclusive scan of the per-expert counts (one workgroup; each thread owns a
+// contiguous range of experts).
+__global__ __launch_bounds__(1024) void k_offsets(const int32_t* __restrict__ counts, int E,
+                                                  int32_t* __restrict__ offsets) {
     const int per = (E + blockDim.x - 1) / blockDim.x;
     const int e0 = threadIdx.x * per;
     int32_t local = 0;
-    for (int e = e0; e < e0 + per && e < E; ++e) local += tot[e];
+    for (int e = e0; e < e0 + per && e < E; ++e) local += counts[e];
     int32_t total;
     int32_t run = block_exclusive_scan<int32_t>(local, &total);
     for (int e = e0; e < e0 + per && e < E; ++e) {
         offsets[e] = run;
-        run += tot[e];
+        run += counts[e];
     }
     if (threadIdx.x == 0) offsets[E] = total;
 }
 
 __global__ __launch_bounds__(kDispatchChunk) void k_permute(const int32_t* __restrict__ ids, int64_t NK, int E,
-                                                            const int32_t* __restrict__ chunk_base,
+                                                            int nchunks, const int32_t* __restrict__ chunk_base,
                                                             const int32_t* __restrict__ offsets,
                                                             int32_t* __restrict__ sorted_slot,
                                                             int32_t* __restrict__ slot_pos) {
@@ -113,7 +130,7 @@ __global__ __launch_bounds__(kDispatchChunk) void k_permute(const int32_t* __res
     }
     int rank = 0;
     for (int j = 0; j < (int)threadIdx.x; ++j) rank += (sid[j] == e);
-    const int32_t p = offsets[e] + chunk_base[(int64_t)blockIdx.x * E + e] + rank;
+    const int32_t p = offsets[e] + chunk_base[(int64_t)e * nchunks + blockIdx.x] + rank;
     sorted_slot[p] = (int32_t)s;
     slot_pos[s] = p;
 }
@@ -130,14 +147,17 @@ hipError_t launch_dispatch(const int32_t* ids, int64_t N, int K, int E, int32_t*
     const int64_t NK = N * K;
     const int nchunks = (int)((NK + kDispatchChunk - 1) / kDispatchChunk);
     if (checked) hipLaunchKernelGGL(k_fill_i32, dim3(1), dim3(64), 0, stream, err_flag, (int64_t)1, 0);
-    if (nchunks > 0)
+    if (nchunks > 0) {
         hipLaunchKernelGGL(k_hist, dim3(nchunks), dim3(kDispatchChunk), E * sizeof(int32_t), stream, ids, NK,
-                           K, E, chunk_counts, err_flag, checked ? 1 : 0);
-    hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), E * sizeof(int32_t), stream, chunk_counts, nchunks, E,
-                       counts, offsets);
+                           K, E, nchunks, chunk_counts, err_flag, checked ? 1 : 0);
+        hipLaunchKernelGGL(k_colscan, dim3((E + 3) / 4), dim3(256), 0, stream, chunk_counts, nchunks, E, counts);
+    } else {
+        hipLaunchKernelGGL(k_fill_i32, dim3((E + 255) / 256), dim3(256), 0, stream, counts, (int64_t)E, 0);
+    }
+    hipLaunchKernelGGL(k_offsets, dim3(1), dim3(1024), 0, stream, counts, E, offsets);
     if (nchunks > 0)
-        hipLaunchKernelGGL(k_permute, dim3(nchunks), dim3(kDispatchChunk), 0, stream, ids, NK, E, chunk_counts,
-                           offsets, sorted_slot, slot_pos);
+        hipLaunchKernelGGL(k_permute, dim3(nchunks), dim3(kDispatchChunk), 0, stream, ids, NK, E, nchunks,
+                           chunk_counts, offsets, sorted_slot, slot_pos);
     return hipGetLastError();
 }
 

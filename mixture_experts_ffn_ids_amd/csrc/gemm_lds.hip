@@ -43,8 +43,8 @@
 // the row tiles that share a weight block, and the n-blocks that share a tile's rows, run
 // on the same XCD at about the same time and share its L2.
 //
-// Epilogue: results are staged through the (then idle) stage buffers and written with
-// coalesced 16-byte stores.
+// Epilogue: down results are staged through the (then idle) stage buffers and written with
+// coalesced 16-byte stores; gate|up codes go from registers straight to global memory.
 #include <type_traits>
 
 #include "moe_internal.h"
@@ -55,7 +55,6 @@ namespace {
 
 constexpr int kXcds = 8;
 constexpr int kOutPitch = 256 + 8;  // bf16 elements per row of the staged down-GEMM output
-constexpr int kCodePitch = 144;     // bytes per row of the staged gate|up codes
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
@@ -77,7 +76,7 @@ struct Cfg {
     static constexpr int S_L = BM / ROLE_W;       // row scales copied by each A-wave (one copy)
     static constexpr int S_STAGE = ROLE_W * 64;   // floats per row-scale stage (64 per A-wave)
     static constexpr int STAGES = NA * A_BYTES + NBS * B_BYTES;
-    static constexpr int OUT_BYTES = MODE == 1 ? BM * kOutPitch * 2 : BM * kCodePitch + 4 * BM * 4;
+    static constexpr int OUT_BYTES = MODE == 1 ? BM * kOutPitch * 2 : 4 * BM * 4;
     static constexpr int MAIN = STAGES > OUT_BYTES ? STAGES : OUT_BYTES;
     static constexpr int MAX_KB = 65536 / 128;    // K blocks at the largest supported K
     // LDS: A stages | B stages (or the output tile) | row scales [NA][S_STAGE] | source rows
@@ -427,9 +426,10 @@ __global__ __launch_bounds__(512) void k_gemm_lds(const LdsGemmParams P) {
     // acc[mt][j][i]: row rb + rlane of the tile (rb = wm MT 16 + 16 mt), weight row
     // bbase[j] + 4 kg + i of the workgroup's 256
     if constexpr (MODE == 0) {
-        // ---- h = silu(g) * u, per-row amax over the 128 columns, e4m3 requantisation
-        uint8_t* out = smem;                                          // [BM][kCodePitch] codes
-        float* sRed = reinterpret_cast<float*>(smem + BM * kCodePitch); // [4][BM] row maxima
+        // ---- h = silu(g) * u, per-row amax over the 128 columns, e4m3 requantisation; each
+        // lane stores its 4 consecutive codes per subtile straight from registers (measured
+        // faster here than staging the 24-KB code tile through LDS)
+        float* sRed = reinterpret_cast<float*>(smem);                 // [4][BM] row maxima
         float h[MT][2][4];
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
@@ -457,20 +457,16 @@ __global__ __launch_bounds__(512) void k_gemm_lds(const LdsGemmParams P) {
 #pragma unroll
             for (int k = 0; k < 8; ++k) q[k] = h[mt][k >> 2][k & 3];
             scale_group(q, sc);
+            if (row < nrows) {
+                const int64_t p = p0 + row;
 #pragma unroll
-            for (int jj = 0; jj < 2; ++jj) {
-                const uint32_t lo = f32x2_to_e4m3(q[4 * jj], q[4 * jj + 1]);
-                const uint32_t hi = f32x2_to_e4m3(q[4 * jj + 2], q[4 * jj + 3]);
-                *reinterpret_cast<uint32_t*>(out + row * kCodePitch + wn * 32 + jj * 16 + 4 * kg) = lo | (hi << 16);
+                for (int jj = 0; jj < 2; ++jj) {
+                    const uint32_t lo = f32x2_to_e4m3(q[4 * jj], q[4 * jj + 1]);
+                    const uint32_t hi = f32x2_to_e4m3(q[4 * jj + 2], q[4 * jj + 3]);
+                    *reinterpret_cast<uint32_t*>(P.hq + p * P.Ndim + n0 + wn * 32 + jj * 16 + 4 * kg) = lo | (hi << 16);
+                }
+                if (wn == 0 && kg == 0) P.hs[p * NB128 + nb] = sc;
             }
-            if (wn == 0 && kg == 0 && row < nrows) P.hs[(p0 + row) * NB128 + nb] = sc;
-        }
-        __syncthreads();
-        for (int c = tid; c < BM * 8; c += C::THREADS) {
-            const int row = c >> 3;
-            if (row < nrows)
-                *reinterpret_cast<uint4*>(P.hq + (p0 + row) * P.Ndim + n0 + (c & 7) * 16) =
-                    *reinterpret_cast<const uint4*>(out + row * kCodePitch + (c & 7) * 16);
         }
     } else {
         // ---- bf16 Y tile [BM][256] through LDS, coalesced 16-B stores of valid rows/columns

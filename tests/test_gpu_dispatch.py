@@ -45,6 +45,8 @@ def test_dispatch_edge_cases():
     _assert_same(np.argsort(rng.random((3, 8192)), 1)[:, :8].astype(np.int32), 8192)   # E at the limit
     _assert_same(np.argsort(rng.random((5000, 64)), 1)[:, :8].astype(np.int32), 64)    # many chunks
     _assert_same(np.argsort(rng.random((31, 64)), 1)[:, :64].astype(np.int32), 64)     # K = 64 (limit)
+    _assert_same(np.argsort(rng.random((333, 5)), 1).astype(np.int32), 5)              # E not a multiple of 4,
+    _assert_same(np.argsort(rng.random((4999, 7)), 1)[:, :3].astype(np.int32), 7)     # ragged last chunk
 
 
 def test_dispatch_empty():

@@ -71,6 +71,12 @@ def test_skew_multiple_row_tiles():
     _check_small(cfg, ids, w)
 
 
+def test_many_choices_per_token():
+    # K = 12 > 8: the combine's second batch of source rows, part-filled; d = 1536: the second
+    # 1024-column slice of a token covers only half a wave; with the shared expert
+    _check_small(Config("k12", 40, 1536, 1024, 16, 12, "rmsnorm", "uniform", "dirichlet", True, seed=12))
+
+
 def test_empty_experts_and_single_token():
     cfg = Config("sparse", 4, 256, 1024, 64, 2, "normal", "uniform", "uniform", False, seed=5)
     _check_small(cfg)

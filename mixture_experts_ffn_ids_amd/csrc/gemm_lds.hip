@@ -216,34 +216,6 @@ __global__ __launch_bounds__(512) void k_gemm_lds(const LdsGemmParams P) {
     const int NB128 = P.Ndim / 128;
     const int n0 = MODE == 0 ? nb * 128 : nb * 256;
 
-    // source row of every tile row; rows past the end repeat the tile's first row
-    for (int r = tid; r < BM; r += C::THREADS) {
-        const int64_t p = p0 + (r < nrows ? r : 0);
-        int32_t src;
-        if (MODE == 0) {
-            int64_t tok = P.gather[p] / P.K_top;
-            tok = tok < 0 ? 0 : (tok >= P.src_rows ? P.src_rows - 1 : tok);
-            src = (int32_t)tok;
-        } else {
-            src = (int32_t)p;
-        }
-        sRow[r] = src;
-    }
-    // weight block scales of the workgroup's columns for every K block: gate|up -> gate and
-    // up scales of d_ff block nb; down -> the two 128-column blocks of n-block nb
-    for (int i = tid; i < 2 * KB; i += C::THREADS) {
-        const int which = i / KB, kb = i % KB;
-        float v;
-        if (MODE == 0) {
-            v = (which == 0 ? P.s0 : P.s1)[((int64_t)e * NB128 + nb) * KB + kb];
-        } else {
-            const int cb = n0 / 128 + which;
-            v = cb < NB128 ? P.s0[((int64_t)e * NB128 + cb) * KB + kb] : 0.0f;
-        }
-        sSw[which * C::MAX_KB + kb] = v;
-    }
-    __syncthreads();
-
     // ---- per-lane copy plan. Wave copy q fills rows 8q .. 8q+7 of a stage; lane L lands in
     // row 8q + (L >> 3), slot L & 7, which holds logical chunk (L & 7) ^ (L >> 3) ^ (q & 1).
     // A-wave w (0..3) makes copies q = w + 4i of the activations, B-wave w (4..7) copies
@@ -257,9 +229,8 @@ __global__ __launch_bounds__(512) void k_gemm_lds(const LdsGemmParams P) {
     const uint8_t* const wBase1 = (MODE == 0 ? P.w1 : P.w0) + (int64_t)e * P.Ndim * P.Kdim;
     // row scales: lane L < S_L of A-wave rw copies the scale of slot rw * S_L + L into position
     // rw * 64 + L of a stage; the other lanes copy a valid value into the padding (so the copy
-    // needs no branch)
-    const uint32_t sOff =
-        lane < C::S_L ? (uint32_t)sRow[scale_slot_row<MT>(rw * C::S_L + lane)] * (uint32_t)KB * 4u : 0u;
+    // needs no branch). Set once the source rows are in LDS.
+    uint32_t sOff = 0;
     const uint32_t ldsA = lds_addr(sA) + rw * 1024, ldsB = lds_addr(sB) + rw * 1024;
     const uint32_t ldsS = lds_addr(sSA) + rw * 256;
 
@@ -305,10 +276,15 @@ __global__ __launch_bounds__(512) void k_gemm_lds(const LdsGemmParams P) {
             }
         };
         uint32_t cIdx[KEEP_OFF ? NQ : 1];
-        if constexpr (KEEP_OFF) {
+        auto plan = [&]() {
+            if constexpr (KEEP_OFF) {
 #pragma unroll
-            for (int i = 0; i < NQ; ++i) cIdx[i] = (!BW && i == C::A_Q) ? 0u : off(i);
-        }
+                for (int i = 0; i < NQ; ++i) cIdx[i] = (!BW && i == C::A_Q) ? 0u : off(i);
+            }
+            if constexpr (!BW)
+                sOff = lane < C::S_L ? (uint32_t)sRow[scale_slot_row<MT>(rw * C::S_L + lane)] * (uint32_t)KB * 4u
+                                     : 0u;
+        };
         auto get_off = [&](int i) -> uint32_t {
             if constexpr (KEEP_OFF) return cIdx[i]; else return off(i);
         };
@@ -388,8 +364,49 @@ __global__ __launch_bounds__(512) void k_gemm_lds(const LdsGemmParams P) {
         // of iteration kb, block kb+1 must have landed; what a wave may leave in flight then
         // is the copies it issued last, so an in-order count of pending copies is an exact
         // wait. Both roles pass the same number of barriers.
-        issue(0, 0, NQ);
-        if (NR == 3 && KB > 1) issue(1, 0, NQ);
+        // Prologue. The weights' first blocks depend only on the tile, so B-waves issue them
+        // at once; meanwhile the A-waves (no copies in flight yet, so their loads cost no
+        // extra waits) fill the tables of source rows and weight block scales, and after the
+        // barrier that publishes them they issue the activations' first blocks.
+        if constexpr (BW) {
+            plan();
+            issue(0, 0, NQ);
+            if (NR == 3 && KB > 1) issue(1, 0, NQ);
+        } else {
+            // source row of every tile row; rows past the end repeat the tile's first row
+            for (int r = tid; r < BM; r += C::ROLE_W * 64) {
+                const int64_t p = p0 + (r < nrows ? r : 0);
+                int32_t src;
+                if (MODE == 0) {
+                    int64_t tok = P.gather[p] / P.K_top;
+                    tok = tok < 0 ? 0 : (tok >= P.src_rows ? P.src_rows - 1 : tok);
+                    src = (int32_t)tok;
+                } else {
+                    src = (int32_t)p;
+                }
+                sRow[r] = src;
+            }
+            // weight block scales of the workgroup's columns for every K block: gate|up ->
+            // gate and up scales of d_ff block nb; down -> the two 128-column blocks of n-block
+            // nb
+            for (int i = tid; i < 2 * KB; i += C::ROLE_W * 64) {
+                const int which = i / KB, kb = i % KB;
+                float v;
+                if (MODE == 0) {
+                    v = (which == 0 ? P.s0 : P.s1)[((int64_t)e * NB128 + nb) * KB + kb];
+                } else {
+                    const int cb = n0 / 128 + which;
+                    v = cb < NB128 ? P.s0[((int64_t)e * NB128 + cb) * KB + kb] : 0.0f;
+                }
+                sSw[which * C::MAX_KB + kb] = v;
+            }
+        }
+        __syncthreads();
+        if constexpr (!BW) {
+            plan();
+            issue(0, 0, NQ);
+            if (NR == 3 && KB > 1) issue(1, 0, NQ);
+        }
         wait_pending(NR == 3 && KB > 1 ? NQ : 0);
         __syncthreads();
 

@@ -41,7 +41,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="k2_decode_256")
     ap.add_argument("--cpu-tokens", type=int, default=None,
-                    help="tokens in the oracle's CPU-baseline sample (default: whole batch up to 256)")
+                    help="rows of x in the oracle's CPU-baseline sample (default: whole batch up to 2048 / top_k)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--tile", choices=["auto", "16", "128", "192", "256"], default="auto",
                     help="force the grouped GEMMs' tile height (default: chosen from rows per expert)")
@@ -177,7 +177,15 @@ def main():
     layer_bytes = (touched + n_sh) * 3 * (w_proj + s_proj) + 4 * N * d + 8 * N * K
     layer_flops = 2.0 * 3 * d * d_ff * (N * K + n_sh * N)
 
-    tokens_per_s = N / (ms_per_step / 1e3)
+    # the kernel's bound: HBM unless its arithmetic intensity is above the machine's ridge point
+    mfma_bound = gu_flops_per_launch / gu_bytes_per_launch > FP8_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    if mfma_bound:
+        roof = {"bound": "mfma", "achieved": round(achieved_tflops, 1), "peak": FP8_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved_tflops / FP8_PEAK_TFLOPS, 4)}
+    else:
+        roof = {"bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved_gbs / HBM_PEAK_GBS, 4)}
+    tokens_per_s = cfg.layer_tokens / (ms_per_step / 1e3)
     result = {
         "metric": "MoE-layer tokens/s at K2 shapes",
         "value": round(tokens_per_s, 2),
@@ -191,12 +199,14 @@ def main():
         "vs_baseline": None,
         "dtype": "fp8-e4m3 x fp8-e4m3 -> fp32 (bf16 in/out)",
         "data": "synthetic (seeded; random-init fp8 expert weights, 128x128 block scales)",
-        "config": {"workload": cfg.name, "tile": args.tile, "tokens": N, "d": d, "d_ff": d_ff, "experts": E, "top_k": K,
-                   "shared_expert": bool(cfg.shared), "experts_touched": touched},
-        "roofline": {"bound": "hbm", "kernel": "grouped gate|up GEMM (+silu*up requant)",
-                     "achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved_gbs / HBM_PEAK_GBS, 4), "traffic": stored_traffic(cfg.name),
+        "config": {"workload": cfg.name, "tile": args.tile, "tokens": cfg.layer_tokens, "rows": N * K, "d": d,
+                   "d_ff": d_ff, "experts": E, "top_k": K, "shared_expert": bool(cfg.shared),
+                   "experts_touched": touched},
+        "roofline": {**roof, "traffic": stored_traffic(cfg.name),
+                     "kernel": "grouped gate|up GEMM (+silu*up requant)",
                      "algorithmic_bytes_per_launch": int(gu_bytes_per_launch),
+                     "algorithmic_flops_per_launch": gu_flops_per_launch,
+                     "achieved_gbs": round(achieved_gbs, 1), "achieved_tflops": round(achieved_tflops, 1),
                      "avg_launch_ms": gu["avg_ms"]},
         "layer": {"hbm_frac": round(layer_bytes / (ms_per_step / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
                   "fp8_mfma_frac": round(layer_flops / (ms_per_step / 1e3) / 1e12 / FP8_PEAK_TFLOPS, 4),
@@ -205,11 +215,16 @@ def main():
         "kernels": per_kernel,
     }
 
+    if cfg.shard_topk:
+        result["config"]["shard"] = (f"one GPU's part of an expert-parallel layer: {N} received rows (token "
+                                     f"choices of a top-{cfg.shard_topk} router) over its {E} local experts, "
+                                     f"sorted, run and put back in arrival order; tokens = rows / "
+                                     f"{cfg.shard_topk}; the exchanges between GPUs are not part of the step")
     # ---- CPU baseline: the oracle as it stands, on a bounded sample of the same batch
     if not args.no_cpu_baseline:
         import oracle
         from workloads.gen import experts_to_host
-        n_cpu = args.cpu_tokens or min(N, 256)
+        n_cpu = args.cpu_tokens or min(N, 2048 // K)   # about 2048 expert evaluations per pass
         tok = np.arange(n_cpu, dtype=np.int64)
         exh = experts_to_host(experts, np.unique(ids[tok]))
         shh = experts_to_host(shared) if shared is not None else None
@@ -225,10 +240,12 @@ def main():
             dt = time.perf_counter() - t0
             if dt >= 10.0 or passes >= 32:
                 break
-        result["cpu_baseline"] = {"value": round(passes * n_cpu / dt, 3), "unit": "tokens/s", "cores": used,
+        per_row = cfg.layer_tokens / N                # layer tokens per row of x
+        result["cpu_baseline"] = {"value": round(passes * n_cpu * per_row / dt, 3), "unit": "tokens/s",
+                                  "cores": used,
                                   "kind": "oracle",
-                                  "sample": f"{passes} passes over the first {n_cpu} of {N} tokens of the same "
-                                            f"batch, {dt:.1f} s"}
+                                  "sample": f"{passes} passes over the first {n_cpu} of the {N} rows of x in the "
+                                            f"same batch, {dt:.1f} s"}
     del out
     print(json.dumps(result), flush=True)
 

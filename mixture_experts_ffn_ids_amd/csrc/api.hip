@@ -78,16 +78,25 @@ public:
         if (!g_prof_on) return;
         a_ = prof_event();
         b_ = prof_event();
-        if (a_ && b_) hipEventRecord(a_, s_);
+        if (!a_ || !b_ || hipEventRecord(a_, s_) != hipSuccess) release();
     }
     ~ProfScope() {
         std::lock_guard<std::mutex> lk(g_prof_mu);
         if (!a_ || !b_) return;
-        hipEventRecord(b_, s_);
+        if (hipEventRecord(b_, s_) != hipSuccess) {  // this launch goes untimed
+            release();
+            return;
+        }
         g_prof_pending.push_back({kind_, a_, b_});
     }
 
 private:
+    // return the events to the pool (caller holds g_prof_mu)
+    void release() {
+        if (a_) g_prof_pool.push_back(a_);
+        if (b_) g_prof_pool.push_back(b_);
+        a_ = b_ = nullptr;
+    }
     int kind_;
     hipStream_t s_;
     hipEvent_t a_ = nullptr, b_ = nullptr;
@@ -149,7 +158,10 @@ TileShape choose_shape(int64_t N, int64_t rows, int32_t E, int32_t d, int32_t d_
     const int64_t per = touched > 0 ? rows / touched : 0;  // expected rows per touched expert
     if (per < 24) return TileShape::Rows16;
     if (per < 112) return TileShape::Rows128;
-    if (per < 184) return TileShape::Rows192;
+    // 256-row tiles only where one of them holds an expert's rows that would need two
+    // 192-row tiles; experts with more rows than that run faster in 192-row tiles, whose
+    // deeper weight ring fits in LDS
+    if (per < 184 || per > 256) return TileShape::Rows192;
     return TileShape::Rows256;
 }
 

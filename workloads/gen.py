@@ -9,7 +9,7 @@ Recipes (all seeded; seed 0 unless a test picks another):
     K of a uniformly random permutation) or Zipf(1.2) without replacement over
     a seeded permutation of the experts (Gumbel top-K on log r^-1.2);
   * routing weights w[N, K]: softmax of N(0,1) logits, U(0,1) normalised to
-    sum 1, or Dirichlet(1);
+    sum 1, Dirichlet(1), or all ones (a shard's unweighted rows);
   * expert weights: W ~ 0.02 N(0,1) in float32 per projection, one scale per
     128 x 128 block s = blockmax / 448, codes = e4m3(W / s) through torch's
     float8_e4m3fn cast (a library codec, independent of both the oracle's and
@@ -83,6 +83,8 @@ def make_routing(cfg: Config, seed: int | None = None):
         w = u / u.sum(axis=1, keepdims=True)
     elif cfg.w_mode == "dirichlet":
         w = rw.dirichlet(np.ones(K), size=N)
+    elif cfg.w_mode == "ones":
+        w = np.ones((N, K))
     else:
         raise ValueError(cfg.w_mode)
     return ids, np.ascontiguousarray(w.astype(np.float32))

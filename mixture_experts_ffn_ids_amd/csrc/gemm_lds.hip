@@ -34,7 +34,8 @@
 // Rows are 128 B with 16-B chunks XOR-swizzled so that fragment reads are free of bank
 // conflicts. Row scales are stored so that the MT scales one lane needs are adjacent.
 // Rows past the end of the tile copy a valid row (the tile's first row, or the last weight
-// row); they are computed but never stored. The copies are written as inline assembly so
+// row) and are never stored; a wave skips the matrix work of its row subtiles that hold no
+// row of the tile. The copies are written as inline assembly so
 // that the compiler does not wait for them at every LDS read; completion is awaited
 // explicitly (s_waitcnt vmcnt) before the barrier that publishes a block.
 //
@@ -247,6 +248,10 @@ __global__ __launch_bounds__(512) void k_gemm_lds(const LdsGemmParams P) {
         for (int j = 0; j < 4; ++j) acc[mt][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
     const int rlane = lane & 15, kg = lane >> 4;
+    // row subtiles of this wave that hold rows of the tile (uniform per wave): the matrix
+    // work of the others is skipped, their copies still run (they keep the waits exact)
+    int live_mt = (nrows - wm * MT * 16 + 15) / 16;
+    live_mt = __builtin_amdgcn_readfirstlane(live_mt < 0 ? 0 : (live_mt > MT ? MT : live_mt));
     // weight block scale table of the wave's columns: gate|up subtiles 0,1 gate (table 0),
     // 2,3 up (table 1); down: the wave's 64 columns lie in 128-column block wn >> 1
     const int wtab0 = MODE == 0 ? 0 : (wn >> 1);
@@ -258,8 +263,10 @@ __global__ __launch_bounds__(512) void k_gemm_lds(const LdsGemmParams P) {
 
     // The K loop, instantiated per copy role (BW: this wave copies weights) so that the
     // copies it issues between the matrix ops are straight-line code.
-    auto run = [&](auto role) {
+    // FULL: every row subtile of the wave is live, and the matrix work has no branches
+    auto run = [&](auto role, auto full) {
         constexpr bool BW = decltype(role)::value;
+        constexpr bool FULL = decltype(full)::value;
         constexpr int NQ = BW ? C::B_Q : C::A_Q + 1;  // copies per block (A: rows + scales)
         constexpr int NR = BW ? NBS : NA;             // ring depth
         constexpr bool KEEP_OFF = true;               // offsets held in registers
@@ -345,14 +352,16 @@ __global__ __launch_bounds__(512) void k_gemm_lds(const LdsGemmParams P) {
                 }
                 const float f0 = sa[mt] * w0;
                 const float f1 = MODE == 0 ? sa[mt] * w1 : f0;
+                if (FULL || mt < live_mt) {
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const v4f r = mfma_16x16x128_fp8(bf[j], af);
-                    const float f = (MODE == 0 && j >= 2) ? f1 : f0;
-                    acc[mt][j][0] += f * r[0];
-                    acc[mt][j][1] += f * r[1];
-                    acc[mt][j][2] += f * r[2];
-                    acc[mt][j][3] += f * r[3];
+                    for (int j = 0; j < 4; ++j) {
+                        const v4f r = mfma_16x16x128_fp8(bf[j], af);
+                        const float f = (MODE == 0 && j >= 2) ? f1 : f0;
+                        acc[mt][j][0] += f * r[0];
+                        acc[mt][j][1] += f * r[1];
+                        acc[mt][j][2] += f * r[2];
+                        acc[mt][j][3] += f * r[3];
+                    }
                 }
                 __builtin_amdgcn_sched_barrier(0);
                 if (mt + 1 < MT) af = af_next;
@@ -435,10 +444,18 @@ __global__ __launch_bounds__(512) void k_gemm_lds(const LdsGemmParams P) {
         drain(std::integral_constant<int, 0>{});
         if constexpr (AHEAD > 1) drain(std::integral_constant<int, 1>{});
     };
-    if (b_wave)
-        run(std::true_type{});
-    else
-        run(std::false_type{});
+    // every variant passes the same barriers, so the waves of one workgroup may differ
+    if (live_mt == MT) {
+        if (b_wave)
+            run(std::true_type{}, std::true_type{});
+        else
+            run(std::false_type{}, std::true_type{});
+    } else {
+        if (b_wave)
+            run(std::true_type{}, std::false_type{});
+        else
+            run(std::false_type{}, std::false_type{});
+    }
 
     // acc[mt][j][i]: row rb + rlane of the tile (rb = wm MT 16 + 16 mt), weight row
     // bbase[j] + 4 kg + i of the workgroup's 256

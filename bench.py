@@ -17,6 +17,9 @@ quantised product it writes.
 
 The CPU baseline is the plain oracle (test infrastructure) on a bounded sample of
 the same batch, on this host's cores.
+
+With --graph the step is also captured once in a HIP graph and replayed; its time is
+reported under "graph" (the headline value and the kernel timings stay eager).
 """
 from __future__ import annotations
 
@@ -45,6 +48,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--tile", choices=["auto", "16", "128", "192", "256"], default="auto",
                     help="force the grouped GEMMs' tile height (default: chosen from rows per expert)")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the step captured in a HIP graph (replays; reported under \"graph\")")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="instead of the layer, run a plain device-to-device copy of this many bytes "
                          "(5 launches): the reference for scaling rocprofv3's HBM byte counters")
@@ -151,6 +156,33 @@ def main():
     total_ms = start.elapsed_time(end)
     ms_per_step = total_ms / args.steps
 
+    graph_result = None
+    if args.graph:
+        # the same step captured once in a HIP graph (the eager runs above sized the workspaces),
+        # replayed W times untimed and K times timed
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        for _ in range(args.warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+        g0 = torch.cuda.Event(enable_timing=True)
+        g1 = torch.cuda.Event(enable_timing=True)
+        g0.record()
+        for _ in range(args.steps):
+            graph.replay()
+        g1.record()
+        torch.cuda.synchronize()
+        g_ms = g0.elapsed_time(g1) / args.steps
+        graph_result = {"ms_per_step": round(g_ms, 4), "tokens_per_s": round(cfg.layer_tokens / (g_ms / 1e3), 2)}
+        del graph
+
     per_kernel = {}
     for name, kind in (("quant", moe.KERNEL_QUANT), ("dispatch", moe.KERNEL_DISPATCH),
                        ("gate_up", moe.KERNEL_GATE_UP), ("down", moe.KERNEL_DOWN),
@@ -215,6 +247,8 @@ def main():
         "kernels": per_kernel,
     }
 
+    if graph_result is not None:
+        result["graph"] = graph_result
     if cfg.shard_topk:
         result["config"]["shard"] = (f"one GPU's part of an expert-parallel layer: {N} received rows (token "
                                      f"choices of a top-{cfg.shard_topk} router) over its {E} local experts, "

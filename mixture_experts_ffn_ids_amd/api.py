@@ -45,14 +45,18 @@ def _want(t: torch.Tensor, dtype, name: str, ndim: int | None = None):
 
 
 _WS_CACHE: dict = {}
+_WS_RETIRED: list = []
 
 
 def _workspace(nbytes: int, dev: torch.device, tag: str) -> torch.Tensor:
     """A cached uint8 workspace per (device, purpose), grown as needed. Calls that use the
-    same workspace are ordered on the current stream."""
+    same workspace are ordered on the current stream. A workspace that is outgrown stays
+    allocated: a captured HIP graph may still address it."""
     key = (str(dev), tag)
     ws = _WS_CACHE.get(key)
     if ws is None or ws.numel() < nbytes:
+        if ws is not None:
+            _WS_RETIRED.append(ws)
         ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
         _WS_CACHE[key] = ws
     return ws
@@ -155,7 +159,11 @@ def combine(y_sorted: torch.Tensor, disp: Dispatch, topk_w: torch.Tensor,
 
 def moe_layer(x: torch.Tensor, topk_ids: torch.Tensor, topk_w: torch.Tensor, experts,
               shared_expert=None, flags: int = 0) -> torch.Tensor:
-    """The whole layer: dispatch -> grouped SwiGLU experts -> weighted combine (+ shared expert)."""
+    """The whole layer: dispatch -> grouped SwiGLU experts -> weighted combine (+ shared expert).
+
+    Enqueues kernels only (no host synchronisation, no allocation inside the library), so a
+    call can be captured into a HIP graph (torch.cuda.graph) once it has run eagerly with the
+    same shapes, which sizes the cached workspaces."""
     E = experts.w_gate.shape[0]
     disp = dispatch(topk_ids, E)
     y = grouped_swiglu(x, disp, experts, flags)

@@ -46,6 +46,7 @@
 //
 // Epilogue: down results are staged through the (then idle) stage buffers and written with
 // coalesced 16-byte stores; gate|up codes go from registers straight to global memory.
+#include <atomic>
 #include <type_traits>
 
 #include "moe_internal.h"
@@ -55,6 +56,7 @@ namespace moe {
 namespace {
 
 constexpr int kXcds = 8;
+constexpr int kMaxDevices = 64;     // devices per process the launcher keeps state for
 constexpr int kOutPitch = 256 + 8;  // bf16 elements per row of the staged down-GEMM output
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
@@ -535,12 +537,18 @@ hipError_t launch_lds(const LdsGemmParams& P, int64_t max_tiles, hipStream_t str
     grid = (grid + kXcds - 1) / kXcds * kXcds;
     if (grid <= 0) return hipSuccess;
     if (grid > 0x7fffffff) return hipErrorInvalidValue;
-    static bool attr_set = false;  // raise the dynamic LDS limit once per instantiation
-    if (!attr_set) {
-        hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm_lds<MODE, MT>),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS);
+    // raise the dynamic LDS limit once per instantiation and device (the attribute belongs to
+    // the device's copy of the kernel); concurrent first calls may both set it, which is harmless
+    static std::atomic<bool> attr_set[kMaxDevices];
+    int dev = 0;
+    hipError_t err = hipGetDevice(&dev);
+    if (err != hipSuccess) return err;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    if (!attr_set[dev].load(std::memory_order_acquire)) {
+        err = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm_lds<MODE, MT>),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS);
         if (err != hipSuccess) return err;
-        attr_set = true;
+        attr_set[dev].store(true, std::memory_order_release);
     }
     hipLaunchKernelGGL((k_gemm_lds<MODE, MT>), dim3((unsigned)grid), dim3(C::THREADS), C::LDS, stream, P);
     return hipGetLastError();

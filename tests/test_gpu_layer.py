@@ -143,3 +143,44 @@ def test_k2_config_full_size(cfg):
     shh = experts_to_host(shd) if shd is not None else None
     _, ref64 = oracle.moe_forward(x, ids, w, exh, shh, tokens=tok)
     assert_layer_close(out[tok], ref64, f"{cfg.name} sampled {len(tok)} tokens")
+
+
+# --------------------------------------------------------------------------- size limits
+def test_maximum_hidden_size():
+    # d = 65536 = MOE_MAX_DIM: 512 K blocks per gate|up row, which exactly fills the many-row
+    # kernels' table of weight block scales; every tile height, against the oracle
+    _check_small(Config("max_d", 48, 65536, 256, 4, 2, "normal", "uniform", "softmax", False, seed=31))
+
+
+def test_activation_offsets_beyond_32_bits():
+    """N * d >= 2^32: the many-row kernels' 32-bit activation offsets would overflow, so every
+    tile height must fall back to the 16-row kernel (64-bit addressing). Rows past 2^32 bytes of
+    x, x_q and y_sorted are compared with the oracle."""
+    d, d_ff, E, K = 65536, 128, 2, 1
+    N = 65536 + 16                         # x_q row 65536 starts at byte 2^32
+    cfg = Config("offsets64", N, d, d_ff, E, K, "normal", "uniform", "uniform", False, seed=32)
+    exh = make_experts_host(cfg)
+    exd = experts_dev(exh)
+    ids, w = make_routing(cfg)
+    say("offsets64 inputs")
+    gen = torch.Generator(device="cuda").manual_seed(32)
+    x = torch.empty((N, d), dtype=torch.bfloat16, device="cuda")
+    for r0 in range(0, N, 4096):          # drawn in chunks: float32 staging of the whole x is 17 GB
+        r1 = min(N, r0 + 4096)
+        x[r0:r1] = torch.randn((r1 - r0, d), generator=gen, device="cuda").to(torch.bfloat16)
+    t_ids = torch.from_numpy(ids).cuda()
+    t_w = torch.from_numpy(w).cuda()
+    tok = np.array([0, 32767, 32768, 40000, 65535, 65536, N - 1], np.int64)
+    outs = []
+    for flags in (0, moe.FLAG_TILE_192):
+        say(f"offsets64 layer flags={flags}")
+        out = moe.moe_layer(x, t_ids, t_w, exd, flags=flags)
+        torch.cuda.synchronize()
+        outs.append(bits_host(out[torch.from_numpy(tok).cuda()]))
+        del out
+    assert np.array_equal(outs[0], outs[1])
+    x_tok = bits_host(x[torch.from_numpy(tok).cuda()])
+    del x
+    say(f"offsets64 oracle tokens={len(tok)}")
+    _, ref64 = oracle.moe_forward(x_tok, ids[tok], w[tok], exh)
+    assert_layer_close(outs[0], ref64, "offsets64 sampled")

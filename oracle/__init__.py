@@ -69,7 +69,9 @@ def _load():
         lib.orc_moe_forward.argtypes = [P, i64, i32, P, P, i32, i32, i32,
                                         P, P, P, P, P, P,
                                         P, P, P, P, P, P, i32,
-                                        P, i64, P, P, i32]
+                                        P, P, i64, P, P, i32]
+        lib.orc_rmsnorm_rows.restype = ctypes.c_int
+        lib.orc_rmsnorm_rows.argtypes = [P, P, ctypes.c_float, i64, i64, P]
         lib.orc_expert_rows.restype = ctypes.c_int
         lib.orc_expert_rows.argtypes = [P, i64, i32, i32, i32, P, P, P, P, P, P, P, P, i64, P, P, P, i32]
         lib.orc_threads.restype = ctypes.c_int
@@ -192,8 +194,9 @@ class ExpertWeightsHost:
 
 def moe_forward(x_bits: np.ndarray, ids: np.ndarray, w: np.ndarray, experts: ExpertWeightsHost,
                 shared: ExpertWeightsHost | None = None, tokens: np.ndarray | None = None,
-                threads: int = 0):
-    """Layer output for the given tokens (default all): (bf16 bits [n, d], float64 [n, d])."""
+                threads: int = 0, residual: np.ndarray | None = None):
+    """Layer output for the given tokens (default all): (bf16 bits [n, d], float64 [n, d]).
+    residual (bf16 bits [N, d]) is added after the shared expert, before the rounding."""
     x_bits = np.ascontiguousarray(x_bits, dtype=np.uint16)
     ids = np.ascontiguousarray(ids, dtype=np.int32)
     w = np.ascontiguousarray(w, dtype=np.float32)
@@ -217,11 +220,26 @@ def moe_forward(x_bits: np.ndarray, ids: np.ndarray, w: np.ndarray, experts: Exp
     else:
         sharrs = [None] * 6
         sh_dff = 0
+    if residual is not None:
+        residual = np.ascontiguousarray(residual, dtype=np.uint16)
+        assert residual.shape == (N, d)
     rc = _load().orc_moe_forward(_ptr(x_bits), N, d, _ptr(ids), _ptr(w), K, ex.E, ex.d_ff,
                                  *[_ptr(a) for a in arrs], *[_ptr(a) for a in sharrs], sh_dff,
-                                 _ptr(tokens), n_eval, _ptr(out), _ptr(out64), int(threads))
+                                 _ptr(residual), _ptr(tokens), n_eval, _ptr(out), _ptr(out64),
+                                 int(threads))
     _check(rc)
     return out, out64
+
+
+def rmsnorm_rows(x_bits: np.ndarray, gain_bits: np.ndarray, eps: float) -> np.ndarray:
+    """RMSNorm of bf16 rows [rows, cols] with a bf16 gain [cols]: bf16 bits [rows, cols]."""
+    x_bits = np.ascontiguousarray(x_bits, dtype=np.uint16)
+    gain_bits = np.ascontiguousarray(gain_bits, dtype=np.uint16)
+    rows, cols = x_bits.shape
+    assert gain_bits.shape == (cols,)
+    y = np.empty((rows, cols), np.uint16)
+    _check(_load().orc_rmsnorm_rows(_ptr(x_bits), _ptr(gain_bits), float(eps), rows, cols, _ptr(y)))
+    return y
 
 
 def expert_rows(x_bits: np.ndarray, experts, tokens: np.ndarray, expert_ids: np.ndarray,

@@ -186,6 +186,45 @@ int orc_quant_rows_f32(const float* x, int64_t rows, int64_t cols, uint8_t* q, f
 }
 
 /* ---------------------------------------------------------------------
+ * RMSNorm of bfloat16 rows with a bfloat16 gain per feature, the norm the
+ * block applies before its FFN ("Input features" page, evidence "rmsnorm":
+ * DeepseekV3RMSNorm, computed in float32 and returned in the input dtype,
+ * then scaled by the gain; evidence "block": post_attention_layernorm feeds
+ * the mlp). Per row of length n:
+ *   v   = fl32(mean of x_i^2)              (sum and division in double)
+ *   r   = fl32(1 / sqrt(fl32(v + eps)))    (double, one rounding)
+ *   t_i = bf16(fl32(x_i * r))              (back to the input dtype)
+ *   y_i = bf16(g_i * t_i)                  (g_i * t_i is exact in float32)
+ * The page fixes float32 for the normalisation but neither the summation
+ * order of the mean nor the rounding of the reciprocal square root; these
+ * are the readings taken here. y[rows][cols] bf16 bits.
+ * ------------------------------------------------------------------- */
+int orc_rmsnorm_rows(const uint16_t* x, const uint16_t* gain, float eps, int64_t rows,
+                     int64_t cols, uint16_t* y)
+{
+    if (rows < 0 || cols <= 0)
+        return ORC_ERR_SHAPE;
+    for (int64_t r = 0; r < rows; ++r) {
+        const uint16_t* xr = x + r * cols;
+        double ss = 0.0;
+        for (int64_t i = 0; i < cols; ++i) {
+            double v = (double)orc_bf16_to_float(xr[i]);
+            ss += v * v;
+        }
+        float var = (float)(ss / (double)cols);
+        float t = var + eps;
+        float rs = (float)(1.0 / sqrt((double)t));
+        for (int64_t i = 0; i < cols; ++i) {
+            float xn = orc_bf16_to_float(xr[i]) * rs;
+            float tb = orc_bf16_to_float(orc_bf16_from_double((double)xn));
+            float g = orc_bf16_to_float(gain[i]);
+            y[r * cols + i] = orc_bf16_from_double((double)(g * tb));
+        }
+    }
+    return ORC_OK;
+}
+
+/* ---------------------------------------------------------------------
  * Dispatch ("Mixture of experts" page, Code: moe_infer): count the tokens
  * routed to each expert, order the flat (token, choice) slots s = n*K + k by
  * expert, and keep the inverse so outputs can be scattered back. The pages
@@ -287,6 +326,9 @@ static void expert_forward(const double* xdec, const float* xs, int64_t d, int64
  * wg, wu [E][d_ff][d], sg, su [E][d_ff/128][d/128], wd [E][d][d_ff],
  * sd [E][d/128][d_ff/128]. Shared expert (all NULL to omit) has the same
  * layout with E = 1 and its own intermediate size sh_dff.
+ * residual[N][d] bf16 (NULL to omit): the block's second residual addition
+ * ("Input features" page, evidence "block": hidden = residual + mlp(...)),
+ * added after the shared expert, before the one rounding.
  * tokens: list of token indices to evaluate (NULL = all N, in order);
  * out_bf16[n_eval][d] and, if non-NULL, out_f64[n_eval][d] (before rounding).
  * n_threads <= 0 uses the OpenMP default.
@@ -296,8 +338,8 @@ int orc_moe_forward(const uint16_t* x, int64_t N, int32_t d, const int32_t* ids,
                     const uint8_t* wu, const float* su, const uint8_t* wd, const float* sd,
                     const uint8_t* sh_wg, const float* sh_sg, const uint8_t* sh_wu,
                     const float* sh_su, const uint8_t* sh_wd, const float* sh_sd, int32_t sh_dff,
-                    const int64_t* tokens, int64_t n_eval, uint16_t* out_bf16, double* out_f64,
-                    int32_t n_threads)
+                    const uint16_t* residual, const int64_t* tokens, int64_t n_eval,
+                    uint16_t* out_bf16, double* out_f64, int32_t n_threads)
 {
     if (N < 0 || d <= 0 || d % GROUP || K < 0 || E < 1 || K > E || d_ff <= 0 || d_ff % GROUP)
         return ORC_ERR_SHAPE;
@@ -377,6 +419,9 @@ int orc_moe_forward(const uint16_t* x, int64_t N, int32_t d, const int32_t* ids,
                     for (int64_t o = 0; o < D; ++o)
                         acc[o] += y[o];
                 }
+                if (residual)
+                    for (int64_t o = 0; o < D; ++o)
+                        acc[o] += (double)orc_bf16_to_float(residual[n * D + o]);
                 for (int64_t o = 0; o < D; ++o) {
                     out_bf16[t * D + o] = orc_bf16_from_double(acc[o]);
                     if (out_f64)

@@ -48,6 +48,10 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--tile", choices=["auto", "16", "128", "192", "256"], default="auto",
                     help="force the grouped GEMMs' tile height (default: chosen from rows per expert)")
+    ap.add_argument("--block", action="store_true",
+                    help="time the FFN half of a block around the layer instead: hidden + layer(RMSNorm(hidden)), "
+                         "with the RMSNorm fused into the activation quantisation and the residual addition "
+                         "into the combine")
     ap.add_argument("--graph", action="store_true",
                     help="also time the step captured in a HIP graph (replays; reported under \"graph\")")
     ap.add_argument("--copy-bytes", type=int, default=0,
@@ -135,8 +139,17 @@ def main():
     flags = {"auto": 0, "16": moe.FLAG_TILE_16, "128": moe.FLAG_TILE_128, "192": moe.FLAG_TILE_192,
              "256": moe.FLAG_TILE_256}[args.tile]
 
-    def step():
-        return moe.moe_layer(x, t_ids, t_w, experts, shared, flags=flags)
+    if args.block:
+        from workloads.gen import make_block_inputs
+        h_bits, g_bits = make_block_inputs(cfg)
+        hidden = torch.from_numpy(h_bits.view(np.int16)).view(torch.bfloat16).to(dev)
+        gain = torch.from_numpy(g_bits.view(np.int16)).view(torch.bfloat16).to(dev)
+
+        def step():
+            return moe.moe_block_ffn(hidden, gain, 1e-6, t_ids, t_w, experts, shared, flags=flags)
+    else:
+        def step():
+            return moe.moe_layer(x, t_ids, t_w, experts, shared, flags=flags)
 
     for _ in range(args.warmup):
         step()
@@ -206,7 +219,7 @@ def main():
     gu_avg_s = gu["avg_ms"] / 1e3
     achieved_gbs = gu_bytes_per_launch / gu_avg_s / 1e9
     achieved_tflops = gu_flops_per_launch / gu_avg_s / 1e12
-    layer_bytes = (touched + n_sh) * 3 * (w_proj + s_proj) + 4 * N * d + 8 * N * K
+    layer_bytes = (touched + n_sh) * 3 * (w_proj + s_proj) + 4 * N * d + 8 * N * K + (2 * d if args.block else 0)
     layer_flops = 2.0 * 3 * d * d_ff * (N * K + n_sh * N)
 
     # the kernel's bound: HBM unless its arithmetic intensity is above the machine's ridge point
@@ -249,6 +262,10 @@ def main():
 
     if graph_result is not None:
         result["graph"] = graph_result
+    if args.block:
+        result["config"]["block"] = ("hidden + layer(RMSNorm(hidden)): the block's RMSNorm fused into the "
+                                     "activation quantisation (kernel 'quant'), its residual addition into "
+                                     "the combine")
     if cfg.shard_topk:
         result["config"]["shard"] = (f"one GPU's part of an expert-parallel layer: {N} received rows (token "
                                      f"choices of a top-{cfg.shard_topk} router) over its {E} local experts, "
@@ -269,7 +286,11 @@ def main():
         passes = 0
         t0 = time.perf_counter()
         while True:
-            oracle.moe_forward(x_bits, ids, w, exh, shh, tokens=tok, threads=threads)
+            if args.block:
+                xn = oracle.rmsnorm_rows(h_bits[tok], g_bits, 1e-6)
+                oracle.moe_forward(xn, ids[tok], w[tok], exh, shh, threads=threads, residual=h_bits[tok])
+            else:
+                oracle.moe_forward(x_bits, ids, w, exh, shh, tokens=tok, threads=threads)
             passes += 1
             dt = time.perf_counter() - t0
             if dt >= 10.0 or passes >= 32:

@@ -142,6 +142,28 @@ moe_status moe_grouped_swiglu(const uint16_t* x, int64_t N, int32_t K, int32_t E
                               uint32_t flags, void* stream);
 
 /* ------------------------------------------------------------------------
+ * Grouped SwiGLU experts on activations already quantised: moe_grouped_swiglu
+ * from its second step on, with xq/xs in place of the e4m3 quantisation of x.
+ * For callers that produce the codes elsewhere: moe_rmsnorm_quantize_rows,
+ * which quantises in the same pass as the block's RMSNorm, or one GPU of an
+ * expert-parallel group that receives its tokens' rows already quantised.
+ * xq[N][d] e4m3 codes and xs[N][d/128] float32 scales, laid out and defined
+ * as moe_quantize_rows writes them; other arguments as moe_grouped_swiglu.
+ * With xq, xs = moe_quantize_rows(x), y_sorted equals moe_grouped_swiglu's
+ * bit for bit. The workspace needs moe_swiglu_q_workspace_size bytes (no room
+ * for xq/xs).
+ * ---------------------------------------------------------------------- */
+size_t moe_swiglu_q_workspace_size(int64_t N, int32_t K, int32_t E, int32_t d, int32_t d_ff);
+
+moe_status moe_grouped_swiglu_q(const uint8_t* xq, const float* xs, int64_t N, int32_t K, int32_t E,
+                                int32_t d, int32_t d_ff, const int32_t* offsets,
+                                const int32_t* sorted_slot, const uint8_t* w_gate,
+                                const float* s_gate, const uint8_t* w_up, const float* s_up,
+                                const uint8_t* w_down, const float* s_down, uint16_t* y_sorted,
+                                void* workspace, size_t workspace_bytes, uint32_t flags,
+                                void* stream);
+
+/* ------------------------------------------------------------------------
  * Weighted combine ("Mixture of experts" page, Code: moe_infer's weighted sum
  * over the K outputs of each token, and forward's addition of the shared
  * expert):
@@ -157,6 +179,19 @@ moe_status moe_combine(const uint16_t* y_sorted, const int32_t* slot_pos, const 
                        const uint16_t* shared, int64_t N, int32_t K, int32_t d, uint16_t* out,
                        void* stream);
 
+/* The combine fused with the block's second residual addition ("Input
+ * features" page, evidence "block": the FFN's output is added to the residual
+ * stream it was computed from):
+ *   out[n] = bfloat16( sum_k w[n][k] * y_sorted[slot_pos[n*K+k]] + shared[n]
+ *                      + residual[n] )
+ * in float32, in that order, one rounding. residual[N][d] bf16 is required;
+ * out may be residual itself (the residual stream updated in place), but no
+ * other overlap is allowed. Other arguments as moe_combine. */
+moe_status moe_combine_residual(const uint16_t* y_sorted, const int32_t* slot_pos,
+                                const float* topk_w, const uint16_t* shared,
+                                const uint16_t* residual, int64_t N, int32_t K, int32_t d,
+                                uint16_t* out, void* stream);
+
 /* ------------------------------------------------------------------------
  * Dynamic e4m3 quantisation of bfloat16 rows, one float32 scale per 128
  * consecutive values ("Input features" page, evidence "linear": dynamic
@@ -168,6 +203,24 @@ moe_status moe_combine(const uint16_t* y_sorted, const int32_t* slot_pos, const 
  * ---------------------------------------------------------------------- */
 moe_status moe_quantize_rows(const uint16_t* x, int64_t rows, int32_t cols, uint8_t* q, float* s,
                              void* stream);
+
+/* ------------------------------------------------------------------------
+ * The block's RMSNorm before the FFN, fused with the quantisation of its
+ * output ("Input features" page, evidence "rmsnorm": float32 normalisation,
+ * returned in the input dtype and multiplied by the gain; evidence "linear"
+ * for the e4m3 step). Per row of h[rows][cols] (bf16) with gain[cols] (bf16):
+ *   v   = float32(mean of h_i^2)            (sum and division in double)
+ *   r   = float32(1 / sqrt(float32(v + eps)))  (double, one rounding)
+ *   y_i = bfloat16(gain_i * bfloat16(h_i * r))
+ * then q, s = moe_quantize_rows(y) without storing y unless y is non-NULL
+ * (y[rows][cols] bf16, for a router that reads the normalised features).
+ * q and s feed moe_grouped_swiglu_q. cols: positive multiple of 128, at most
+ * MOE_MAX_DIM; 0 <= rows < 2^31; eps >= 0 and finite. The squares of |h| above
+ * about 1.8e19 would overflow float32 but not the double sum used here.
+ * ---------------------------------------------------------------------- */
+moe_status moe_rmsnorm_quantize_rows(const uint16_t* h, const uint16_t* gain, float eps,
+                                     int64_t rows, int32_t cols, uint16_t* y, uint8_t* q,
+                                     float* s, void* stream);
 
 /* ------------------------------------------------------------------------
  * Diagnostics.

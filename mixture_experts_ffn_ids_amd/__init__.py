@@ -1,13 +1,16 @@
 """MI355X-native routed-expert MoE layer (Kimi-K2 shapes): Python binding of libmoe.
 
 The layer runs entirely in the HIP kernels of libmoe.so (include/moe.h):
-dispatch -> grouped FP8 SwiGLU experts -> deterministic weighted combine.
+dispatch -> grouped FP8 SwiGLU experts -> deterministic weighted combine; moe_block_ffn
+adds the block's RMSNorm (fused with the activation quantisation) and residual addition
+(fused with the combine) around it.
 """
-from .api import (Dispatch, combine, dispatch, grouped_swiglu, identity_dispatch, moe_layer,  # noqa: F401
-                  profile_enable, profile_read, profile_reset, quantize_rows)
+from .api import (Dispatch, combine, dispatch, grouped_swiglu, grouped_swiglu_q, identity_dispatch,  # noqa: F401
+                  moe_block_ffn, moe_layer, profile_enable, profile_read, profile_reset, quantize_rows,
+                  rmsnorm_quantize)
 from ._lib import (FLAG_CHECKED, FLAG_TILE_16, FLAG_TILE_128, FLAG_TILE_192, FLAG_TILE_256, KERNEL_COMBINE,  # noqa: F401
                    KERNEL_DISPATCH, KERNEL_DOWN, KERNEL_GATE_UP, KERNEL_QUANT, LIB_PATH, MoeError)
 
-__all__ = ["Dispatch", "combine", "dispatch", "grouped_swiglu", "identity_dispatch", "moe_layer",
-           "quantize_rows", "profile_enable", "profile_read", "profile_reset", "MoeError", "LIB_PATH",
-           "FLAG_CHECKED", "FLAG_TILE_16", "FLAG_TILE_128", "FLAG_TILE_192", "FLAG_TILE_256"]
+__all__ = ["Dispatch", "combine", "dispatch", "grouped_swiglu", "grouped_swiglu_q", "identity_dispatch",
+           "moe_block_ffn", "moe_layer", "quantize_rows", "rmsnorm_quantize", "profile_enable", "profile_read",
+           "profile_reset", "MoeError", "LIB_PATH", "FLAG_CHECKED", "FLAG_TILE_16", "FLAG_TILE_128", "FLAG_TILE_192", "FLAG_TILE_256"]

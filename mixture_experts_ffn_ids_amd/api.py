@@ -104,11 +104,7 @@ def identity_dispatch(N: int, device) -> Dispatch:
     return dispatch(torch.zeros((N, 1), dtype=torch.int32, device=device), 1)
 
 
-def grouped_swiglu(x: torch.Tensor, disp: Dispatch, experts, flags: int = 0,
-                   out: torch.Tensor | None = None) -> torch.Tensor:
-    """y_sorted [N*K, d] bf16: each sorted row through its expert's SwiGLU MLP (unweighted)."""
-    _want(x, torch.bfloat16, "x", 2)
-    N, d = x.shape
+def _expert_dims(experts, d: int, N: int, disp: Dispatch):
     ex = experts
     for name in ("w_gate", "w_up", "w_down"):
         _want(getattr(ex, name), torch.uint8, name, 3)
@@ -116,17 +112,32 @@ def grouped_swiglu(x: torch.Tensor, disp: Dispatch, experts, flags: int = 0,
         _want(getattr(ex, name), torch.float32, name, 3)
     E, d_ff, d_w = ex.w_gate.shape
     if d_w != d or disp.N != N or disp.E != E:
-        raise ValueError("x, dispatch and expert weights disagree on N, d or E")
+        raise ValueError("activations, dispatch and expert weights disagree on N, d or E")
     if tuple(ex.w_up.shape) != (E, d_ff, d) or tuple(ex.w_down.shape) != (E, d, d_ff):
         raise ValueError("expert weight shapes disagree")
     if (tuple(ex.s_gate.shape) != (E, d_ff // 128, d // 128) or tuple(ex.s_up.shape) != (E, d_ff // 128, d // 128)
             or tuple(ex.s_down.shape) != (E, d // 128, d_ff // 128)):
         raise ValueError("expert scale shapes disagree")
-    K = disp.K
+    return E, d_ff
+
+
+def _y_out(out, rows: int, d: int, device):
     if out is None:
-        out = torch.empty((N * K, d), dtype=torch.bfloat16, device=x.device)
-    else:
-        _want(out, torch.bfloat16, "out", 2)
+        return torch.empty((rows, d), dtype=torch.bfloat16, device=device)
+    _want(out, torch.bfloat16, "out", 2)
+    if tuple(out.shape) != (rows, d):
+        raise ValueError(f"out must be [{rows}, {d}]")
+    return out
+
+
+def grouped_swiglu(x: torch.Tensor, disp: Dispatch, experts, flags: int = 0,
+                   out: torch.Tensor | None = None) -> torch.Tensor:
+    """y_sorted [N*K, d] bf16: each sorted row through its expert's SwiGLU MLP (unweighted)."""
+    _want(x, torch.bfloat16, "x", 2)
+    N, d = x.shape
+    E, d_ff = _expert_dims(experts, d, N, disp)
+    ex, K = experts, disp.K
+    out = _y_out(out, N * K, d, x.device)
     nb = lib().moe_swiglu_workspace_size(N, K, E, d, d_ff)
     ws = _workspace(nb, x.device, "swiglu")
     st = lib().moe_grouped_swiglu(_p(x), N, K, E, d, d_ff, _p(disp.offsets), _p(disp.sorted_slot),
@@ -136,25 +147,70 @@ def grouped_swiglu(x: torch.Tensor, disp: Dispatch, experts, flags: int = 0,
     return out
 
 
+def grouped_swiglu_q(xq: torch.Tensor, xs: torch.Tensor, disp: Dispatch, experts, flags: int = 0,
+                     out: torch.Tensor | None = None) -> torch.Tensor:
+    """grouped_swiglu on activations already quantised: xq [N, d] uint8 e4m3 codes and
+    xs [N, d/128] float32 scales, as quantize_rows or rmsnorm_quantize write them."""
+    _want(xq, torch.uint8, "xq", 2)
+    _want(xs, torch.float32, "xs", 2)
+    N, d = xq.shape
+    if tuple(xs.shape) != (N, d // 128):
+        raise ValueError("xs must be [N, d/128]")
+    E, d_ff = _expert_dims(experts, d, N, disp)
+    ex, K = experts, disp.K
+    out = _y_out(out, N * K, d, xq.device)
+    nb = lib().moe_swiglu_q_workspace_size(N, K, E, d, d_ff)
+    ws = _workspace(nb, xq.device, "swiglu")
+    st = lib().moe_grouped_swiglu_q(_p(xq), _p(xs), N, K, E, d, d_ff, _p(disp.offsets), _p(disp.sorted_slot),
+                                    _p(ex.w_gate), _p(ex.s_gate), _p(ex.w_up), _p(ex.s_up), _p(ex.w_down),
+                                    _p(ex.s_down), _p(out), _p(ws), ws.numel(), int(flags), _stream(xq.device))
+    check(st, "moe_grouped_swiglu_q")
+    return out
+
+
 def combine(y_sorted: torch.Tensor, disp: Dispatch, topk_w: torch.Tensor,
-            shared: torch.Tensor | None = None, out: torch.Tensor | None = None) -> torch.Tensor:
-    """out [N, d] bf16 = sum_k w[n,k] * y_sorted[slot_pos[n*K+k]] (+ shared[n])."""
+            shared: torch.Tensor | None = None, out: torch.Tensor | None = None,
+            residual: torch.Tensor | None = None) -> torch.Tensor:
+    """out [N, d] bf16 = sum_k w[n,k] * y_sorted[slot_pos[n*K+k]] (+ shared[n]) (+ residual[n]).
+    With a residual, out may be the residual tensor itself (updated in place)."""
     _want(y_sorted, torch.bfloat16, "y_sorted", 2)
     _want(topk_w, torch.float32, "topk_w", 2)
     N, K = topk_w.shape
     d = y_sorted.shape[1]
     if disp.N != N or disp.K != K or y_sorted.shape[0] != N * K:
         raise ValueError("combine shapes disagree")
-    if shared is not None:
-        _want(shared, torch.bfloat16, "shared", 2)
-        if tuple(shared.shape) != (N, d):
-            raise ValueError("shared must be [N, d]")
-    if out is None:
-        out = torch.empty((N, d), dtype=torch.bfloat16, device=y_sorted.device)
-    st = lib().moe_combine(_p(y_sorted), _p(disp.slot_pos), _p(topk_w), _p(shared), N, K, d, _p(out),
-                           _stream(y_sorted.device))
-    check(st, "moe_combine")
+    for name, t in (("shared", shared), ("residual", residual)):
+        if t is not None:
+            _want(t, torch.bfloat16, name, 2)
+            if tuple(t.shape) != (N, d):
+                raise ValueError(f"{name} must be [N, d]")
+    out = _y_out(out, N, d, y_sorted.device)
+    if residual is None:
+        st = lib().moe_combine(_p(y_sorted), _p(disp.slot_pos), _p(topk_w), _p(shared), N, K, d, _p(out),
+                               _stream(y_sorted.device))
+        check(st, "moe_combine")
+    else:
+        st = lib().moe_combine_residual(_p(y_sorted), _p(disp.slot_pos), _p(topk_w), _p(shared), _p(residual),
+                                        N, K, d, _p(out), _stream(y_sorted.device))
+        check(st, "moe_combine_residual")
     return out
+
+
+def rmsnorm_quantize(h: torch.Tensor, gain: torch.Tensor, eps: float, keep_normed: bool = False):
+    """The block's RMSNorm of h [rows, cols] bf16 with gain [cols] bf16, fused with its e4m3
+    quantisation: (codes uint8 [rows, cols], scales float32 [rows, cols/128], and the
+    normalised bf16 rows when keep_normed, else None)."""
+    _want(h, torch.bfloat16, "h", 2)
+    _want(gain, torch.bfloat16, "gain", 1)
+    rows, cols = h.shape
+    if gain.shape[0] != cols:
+        raise ValueError("gain must have one entry per column")
+    q = torch.empty((rows, cols), dtype=torch.uint8, device=h.device)
+    s = torch.empty((rows, max(cols // 128, 0)), dtype=torch.float32, device=h.device)
+    y = torch.empty_like(h) if keep_normed else None
+    check(lib().moe_rmsnorm_quantize_rows(_p(h), _p(gain), float(eps), rows, cols, _p(y), _p(q), _p(s),
+                                          _stream(h.device)), "moe_rmsnorm_quantize_rows")
+    return q, s, y
 
 
 def moe_layer(x: torch.Tensor, topk_ids: torch.Tensor, topk_w: torch.Tensor, experts,
@@ -172,6 +228,24 @@ def moe_layer(x: torch.Tensor, topk_ids: torch.Tensor, topk_w: torch.Tensor, exp
         sdisp = identity_dispatch(x.shape[0], x.device)
         shared = grouped_swiglu(x, sdisp, shared_expert)
     return combine(y, disp, topk_w, shared)
+
+
+def moe_block_ffn(hidden: torch.Tensor, gain: torch.Tensor, eps: float, topk_ids: torch.Tensor,
+                  topk_w: torch.Tensor, experts, shared_expert=None, flags: int = 0,
+                  out: torch.Tensor | None = None) -> torch.Tensor:
+    """The FFN half of a MoE block around the layer, with its neighbours fused in:
+    hidden + layer(RMSNorm(hidden)). The RMSNorm runs in the same pass as the activation
+    quantisation and the residual addition in the combine; the routing (ids, weights) is
+    given. Returns the new residual stream (out may be hidden itself)."""
+    E = experts.w_gate.shape[0]
+    xq, xs, _ = rmsnorm_quantize(hidden, gain, eps)
+    disp = dispatch(topk_ids, E)
+    y = grouped_swiglu_q(xq, xs, disp, experts, flags)
+    shared = None
+    if shared_expert is not None:
+        sdisp = identity_dispatch(hidden.shape[0], hidden.device)
+        shared = grouped_swiglu_q(xq, xs, sdisp, shared_expert)
+    return combine(y, disp, topk_w, shared, out=out, residual=hidden)
 
 
 # ---------------------------------------------------------------- profiling

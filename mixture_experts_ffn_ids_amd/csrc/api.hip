@@ -1,6 +1,7 @@
 // C ABI of libmoe: host-side validation, workspace layout, launches and the
 // per-kernel event profiler. The declarations and their contracts are in
 // include/moe.h.
+#include <math.h>
 #include <mutex>
 #include <string.h>
 #include <vector>
@@ -119,12 +120,14 @@ struct SwigluWs {
     size_t xq, xs, hq, hs, tiles, ntiles, total;
     int64_t tile_cap;
 };
-SwigluWs swiglu_layout(int64_t N, int32_t K, int32_t E, int32_t d, int32_t d_ff) {
+// with_x: room for the quantised activations (moe_grouped_swiglu); without it the caller
+// passes them in (moe_grouped_swiglu_q)
+SwigluWs swiglu_layout(int64_t N, int32_t K, int32_t E, int32_t d, int32_t d_ff, bool with_x = true) {
     SwigluWs w;
     const int64_t rows = N * K;
     size_t off = 0;
-    w.xq = off; off = align_up(off + (size_t)N * d);
-    w.xs = off; off = align_up(off + (size_t)N * (d / kGroup) * sizeof(float));
+    w.xq = off; off = with_x ? align_up(off + (size_t)N * d) : off;
+    w.xs = off; off = with_x ? align_up(off + (size_t)N * (d / kGroup) * sizeof(float)) : off;
     w.hq = off; off = align_up(off + (size_t)rows * d_ff);
     w.hs = off; off = align_up(off + (size_t)rows * (d_ff / kGroup) * sizeof(float));
     // sized for the smallest tile height, so every tile shape fits
@@ -230,31 +233,44 @@ size_t moe_swiglu_workspace_size(int64_t N, int32_t K, int32_t E, int32_t d, int
     return swiglu_layout(N, K, E, d, d_ff).total;
 }
 
-moe_status moe_grouped_swiglu(const uint16_t* x, int64_t N, int32_t K, int32_t E, int32_t d, int32_t d_ff,
-                              const int32_t* offsets, const int32_t* sorted_slot, const uint8_t* w_gate,
-                              const float* s_gate, const uint8_t* w_up, const float* s_up,
-                              const uint8_t* w_down, const float* s_down, uint16_t* y_sorted, void* workspace,
-                              size_t workspace_bytes, uint32_t flags, void* stream) {
+size_t moe_swiglu_q_workspace_size(int64_t N, int32_t K, int32_t E, int32_t d, int32_t d_ff) {
+    if (N < 0 || K < 1 || E < 1 || !dim_ok(d) || !dim_ok(d_ff)) return 0;
+    return swiglu_layout(N, K, E, d, d_ff, false).total;
+}
+
+}  // extern "C"
+
+namespace {
+
+// Shared by moe_grouped_swiglu (with_x: x is the bf16 input, quantised into the workspace)
+// and moe_grouped_swiglu_q (xq_in and xs_in are given).
+moe_status grouped_swiglu(bool with_x, const uint16_t* x, const uint8_t* xq_in, const float* xs_in, int64_t N,
+                          int32_t K, int32_t E, int32_t d, int32_t d_ff, const int32_t* offsets,
+                          const int32_t* sorted_slot,
+                          const uint8_t* w_gate, const float* s_gate, const uint8_t* w_up, const float* s_up,
+                          const uint8_t* w_down, const float* s_down, uint16_t* y_sorted, void* workspace,
+                          size_t workspace_bytes, uint32_t flags, void* stream) {
     if (N < 0 || K < 1 || E < 1 || E > MOE_MAX_EXPERTS || K > MOE_MAX_TOPK || K > E || !dim_ok(d) ||
         !dim_ok(d_ff) || N * (int64_t)K > 0x7fffffffLL)
         return MOE_ERR_SHAPE;
     if (N == 0) return MOE_OK;
-    if (!x || !offsets || !sorted_slot || !w_gate || !s_gate || !w_up || !s_up || !w_down || !s_down ||
-        !y_sorted || !workspace)
+    if ((with_x ? !x : (!xq_in || !xs_in)) || !offsets || !sorted_slot || !w_gate || !s_gate || !w_up || !s_up ||
+        !w_down || !s_down || !y_sorted || !workspace)
         return MOE_ERR_NULL;
-    if (!aligned(x, 16) || !aligned(w_gate, 16) || !aligned(w_up, 16) || !aligned(w_down, 16) ||
-        !aligned(y_sorted, 16) || !aligned(workspace, 16) || !aligned(offsets, 4) || !aligned(sorted_slot, 4) ||
-        !aligned(s_gate, 4) || !aligned(s_up, 4) || !aligned(s_down, 4))
+    if ((with_x ? !aligned(x, 16) : (!aligned(xq_in, 16) || !aligned(xs_in, 4))) || !aligned(w_gate, 16) ||
+        !aligned(w_up, 16) || !aligned(w_down, 16) || !aligned(y_sorted, 16) || !aligned(workspace, 16) ||
+        !aligned(offsets, 4) || !aligned(sorted_slot, 4) || !aligned(s_gate, 4) || !aligned(s_up, 4) ||
+        !aligned(s_down, 4))
         return MOE_ERR_ALIGN;
-    const SwigluWs L = swiglu_layout(N, K, E, d, d_ff);
+    const SwigluWs L = swiglu_layout(N, K, E, d, d_ff, with_x);
     if (workspace_bytes < L.total) return MOE_ERR_WORKSPACE;
     moe_status st = check_device();
     if (st != MOE_OK) return st;
 
     hipStream_t s = (hipStream_t)stream;
     uint8_t* ws = (uint8_t*)workspace;
-    uint8_t* xq = ws + L.xq;
-    float* xs = (float*)(ws + L.xs);
+    const uint8_t* xq = with_x ? ws + L.xq : xq_in;
+    const float* xs = with_x ? (const float*)(ws + L.xs) : xs_in;
     uint8_t* hq = ws + L.hq;
     float* hs = (float*)(ws + L.hs);
     Tile* tiles = (Tile*)(ws + L.tiles);
@@ -264,9 +280,9 @@ moe_status moe_grouped_swiglu(const uint16_t* x, int64_t N, int32_t K, int32_t E
     const int BM = tile_rows(shape);
     const int64_t cap = max_tiles(rows, E, BM);
 
-    {
+    if (with_x) {
         ProfScope ps(MOE_KERNEL_QUANT, s);
-        MOE_HIP(launch_quantize_rows(x, N, d, xq, xs, s));
+        MOE_HIP(launch_quantize_rows(x, N, d, ws + L.xq, (float*)(ws + L.xs), s));
     }
     {
         ProfScope ps(MOE_KERNEL_DISPATCH, s);
@@ -290,20 +306,55 @@ moe_status moe_grouped_swiglu(const uint16_t* x, int64_t N, int32_t K, int32_t E
     return MOE_OK;
 }
 
-moe_status moe_combine(const uint16_t* y_sorted, const int32_t* slot_pos, const float* topk_w,
-                       const uint16_t* shared, int64_t N, int32_t K, int32_t d, uint16_t* out, void* stream) {
+moe_status combine(const uint16_t* y_sorted, const int32_t* slot_pos, const float* topk_w, const uint16_t* shared,
+                   const uint16_t* residual, bool need_residual, int64_t N, int32_t K, int32_t d, uint16_t* out,
+                   void* stream) {
     if (N < 0 || K < 1 || K > MOE_MAX_TOPK || !dim_ok(d) || N * (int64_t)K > 0x7fffffffLL) return MOE_ERR_SHAPE;
     if (N == 0) return MOE_OK;
-    if (!y_sorted || !slot_pos || !topk_w || !out) return MOE_ERR_NULL;
-    if (!aligned(y_sorted, 16) || !aligned(out, 16) || (shared && !aligned(shared, 16)) || !aligned(slot_pos, 4) ||
-        !aligned(topk_w, 4))
+    if (!y_sorted || !slot_pos || !topk_w || !out || (need_residual && !residual)) return MOE_ERR_NULL;
+    if (!aligned(y_sorted, 16) || !aligned(out, 16) || (shared && !aligned(shared, 16)) ||
+        (residual && !aligned(residual, 16)) || !aligned(slot_pos, 4) || !aligned(topk_w, 4))
         return MOE_ERR_ALIGN;
     moe_status st = check_device();
     if (st != MOE_OK) return st;
     hipStream_t s = (hipStream_t)stream;
     ProfScope ps(MOE_KERNEL_COMBINE, s);
-    MOE_HIP(launch_combine(y_sorted, slot_pos, topk_w, shared, N, K, d, out, s));
+    MOE_HIP(launch_combine(y_sorted, slot_pos, topk_w, shared, residual, N, K, d, out, s));
     return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_grouped_swiglu(const uint16_t* x, int64_t N, int32_t K, int32_t E, int32_t d, int32_t d_ff,
+                              const int32_t* offsets, const int32_t* sorted_slot, const uint8_t* w_gate,
+                              const float* s_gate, const uint8_t* w_up, const float* s_up,
+                              const uint8_t* w_down, const float* s_down, uint16_t* y_sorted, void* workspace,
+                              size_t workspace_bytes, uint32_t flags, void* stream) {
+    return grouped_swiglu(true, x, nullptr, nullptr, N, K, E, d, d_ff, offsets, sorted_slot, w_gate, s_gate, w_up,
+                          s_up, w_down, s_down, y_sorted, workspace, workspace_bytes, flags, stream);
+}
+
+moe_status moe_grouped_swiglu_q(const uint8_t* xq, const float* xs, int64_t N, int32_t K, int32_t E, int32_t d,
+                                int32_t d_ff, const int32_t* offsets, const int32_t* sorted_slot,
+                                const uint8_t* w_gate, const float* s_gate, const uint8_t* w_up,
+                                const float* s_up, const uint8_t* w_down, const float* s_down,
+                                uint16_t* y_sorted, void* workspace, size_t workspace_bytes, uint32_t flags,
+                                void* stream) {
+    return grouped_swiglu(false, nullptr, xq, xs, N, K, E, d, d_ff, offsets, sorted_slot, w_gate, s_gate, w_up,
+                          s_up, w_down, s_down, y_sorted, workspace, workspace_bytes, flags, stream);
+}
+
+moe_status moe_combine(const uint16_t* y_sorted, const int32_t* slot_pos, const float* topk_w,
+                       const uint16_t* shared, int64_t N, int32_t K, int32_t d, uint16_t* out, void* stream) {
+    return combine(y_sorted, slot_pos, topk_w, shared, nullptr, false, N, K, d, out, stream);
+}
+
+moe_status moe_combine_residual(const uint16_t* y_sorted, const int32_t* slot_pos, const float* topk_w,
+                                const uint16_t* shared, const uint16_t* residual, int64_t N, int32_t K, int32_t d,
+                                uint16_t* out, void* stream) {
+    return combine(y_sorted, slot_pos, topk_w, shared, residual, true, N, K, d, out, stream);
 }
 
 moe_status moe_quantize_rows(const uint16_t* x, int64_t rows, int32_t cols, uint8_t* q, float* s_out,
@@ -317,6 +368,21 @@ moe_status moe_quantize_rows(const uint16_t* x, int64_t rows, int32_t cols, uint
     hipStream_t s = (hipStream_t)stream;
     ProfScope ps(MOE_KERNEL_QUANT, s);
     MOE_HIP(launch_quantize_rows(x, rows, cols, q, s_out, s));
+    return MOE_OK;
+}
+
+moe_status moe_rmsnorm_quantize_rows(const uint16_t* h, const uint16_t* gain, float eps, int64_t rows, int32_t cols,
+                                     uint16_t* y, uint8_t* q, float* s_out, void* stream) {
+    if (rows < 0 || rows > 0x7fffffffLL || !dim_ok(cols) || !(eps >= 0.0f) || eps == INFINITY) return MOE_ERR_SHAPE;
+    if (rows == 0) return MOE_OK;
+    if (!h || !gain || !q || !s_out) return MOE_ERR_NULL;
+    if (!aligned(h, 16) || !aligned(gain, 16) || (y && !aligned(y, 16)) || !aligned(q, 16) || !aligned(s_out, 4))
+        return MOE_ERR_ALIGN;
+    moe_status st = check_device();
+    if (st != MOE_OK) return st;
+    hipStream_t s = (hipStream_t)stream;
+    ProfScope ps(MOE_KERNEL_QUANT, s);
+    MOE_HIP(launch_rmsnorm_quantize(h, gain, eps, rows, cols, y, q, s_out, s));
     return MOE_OK;
 }
 

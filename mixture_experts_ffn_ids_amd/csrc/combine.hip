@@ -1,9 +1,11 @@
 // Weighted combine ("Mixture of experts" page, Code: moe_infer's weighted sum of
-// each token's K expert outputs, and forward's addition of the shared expert):
-//   out[n] = bf16( sum_{k<K} w[n][k] * y_sorted[slot_pos[n*K+k]] + shared[n] )
-// float32, ascending k, shared term last, one nearest-even rounding. Each
-// workgroup owns whole tokens and writes every output element exactly once, so
-// no atomics are needed and the result is deterministic.
+// each token's K expert outputs, and forward's addition of the shared expert), optionally
+// with the block's residual addition ("Input features" page, evidence "block"):
+//   out[n] = bf16( sum_{k<K} w[n][k] * y_sorted[slot_pos[n*K+k]] + shared[n] + residual[n] )
+// float32, ascending k, then the shared term, then the residual, one nearest-even rounding.
+// Each workgroup owns whole tokens and writes every output element exactly once, so no
+// atomics are needed and the result is deterministic. out may be the residual itself: a lane
+// reads each chunk of it before writing that chunk.
 //
 // Memory-bound: a lane moves 8 bf16 (16 B) per source row per chunk; the K source rows
 // of a token are 14 KB contiguous runs at K2 shapes.
@@ -26,7 +28,7 @@ constexpr int kSliceChunks = 128;  // 16-B chunks (8 bf16) per wave slice
 
 __global__ __launch_bounds__(256) void k_combine(const uint16_t* __restrict__ y, const int32_t* __restrict__ slot_pos,
                                                  const float* __restrict__ w, const uint16_t* __restrict__ shared,
-                                                 int64_t N, int K, int d, uint16_t* __restrict__ out) {
+                                                 const uint16_t* residual, int64_t N, int K, int d, uint16_t* out) {
     const int lane = threadIdx.x & 63;
     const int chunks = d / 8;
     const int slices = (chunks + kSliceChunks - 1) / kSliceChunks;
@@ -85,6 +87,12 @@ __global__ __launch_bounds__(256) void k_combine(const uint16_t* __restrict__ y,
 #pragma unroll
             for (int i = 0; i < 8; ++i) acc[j][i] += f[i];
         }
+        if (residual) {
+            float f[8];
+            unpack8(*(reinterpret_cast<const uint4*>(residual + n * d) + c), f);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) acc[j][i] += f[i];
+        }
         uint4 o;
         o.x = f32_to_bf16(acc[j][0]) | (f32_to_bf16(acc[j][1]) << 16);
         o.y = f32_to_bf16(acc[j][2]) | (f32_to_bf16(acc[j][3]) << 16);
@@ -95,12 +103,13 @@ __global__ __launch_bounds__(256) void k_combine(const uint16_t* __restrict__ y,
 }
 
 hipError_t launch_combine(const uint16_t* y, const int32_t* slot_pos, const float* w, const uint16_t* shared,
-                          int64_t N, int K, int d, uint16_t* out, hipStream_t stream) {
+                          const uint16_t* residual, int64_t N, int K, int d, uint16_t* out, hipStream_t stream) {
     if (N == 0) return hipSuccess;
     const int64_t slices = (d / 8 + kSliceChunks - 1) / kSliceChunks;
     const int64_t blocks = (N * slices + 3) / 4;
     if (blocks > 0x7fffffff) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(k_combine, dim3((unsigned)blocks), dim3(256), 0, stream, y, slot_pos, w, shared, N, K, d, out);
+    hipLaunchKernelGGL(k_combine, dim3((unsigned)blocks), dim3(256), 0, stream, y, slot_pos, w, shared, residual, N,
+                       K, d, out);
     return hipGetLastError();
 }
 

@@ -72,6 +72,8 @@ struct GemmPlan;
 
 hipError_t launch_quantize_rows(const uint16_t* x, int64_t rows, int cols, uint8_t* q, float* s,
                                 hipStream_t stream);
+hipError_t launch_rmsnorm_quantize(const uint16_t* x, const uint16_t* gain, float eps, int64_t rows, int cols,
+                                   uint16_t* y, uint8_t* q, float* s, hipStream_t stream);
 
 constexpr int kDispatchChunk = 256;
 hipError_t launch_dispatch(const int32_t* ids, int64_t N, int K, int E, int32_t* counts,
@@ -131,7 +133,7 @@ hipError_t launch_down_lds(const DownArgs& a, int rows, hipStream_t stream);
 
 
 hipError_t launch_combine(const uint16_t* y, const int32_t* slot_pos, const float* w,
-                          const uint16_t* shared, int64_t N, int K, int d, uint16_t* out,
-                          hipStream_t stream);
+                          const uint16_t* shared, const uint16_t* residual, int64_t N, int K, int d,
+                          uint16_t* out, hipStream_t stream);
 
 }  // namespace moe

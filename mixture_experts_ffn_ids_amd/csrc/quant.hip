@@ -65,6 +65,109 @@ __global__ __launch_bounds__(256) void k_quantize_rows(const uint16_t* __restric
     }
 }
 
+// RMSNorm of a bfloat16 row with a bfloat16 gain, fused with the e4m3 quantisation of the
+// result ("Input features" page, evidence "rmsnorm": float32 normalisation, back to the
+// input dtype, then the gain; evidence "linear": dynamic e4m3 per 128 values). One
+// workgroup per row; thread t owns the 16-B chunks t, t + 256, ..., so chunk c is lane c % 16
+// of 128-value group c / 16 in both passes:
+//   pass 1: the sum of squares in double (a bf16 value squared is exact in double), reduced
+//           over the workgroup; v = fp32(sum / cols), r = fp32(1 / sqrt(fp32(v + eps)));
+//   pass 2: t = bf16(x * r), y = bf16(g * t) -- g * t is exact in float32 -- optionally
+//           stored, then quantised exactly as k_quantize_rows does.
+// The first KEEP chunks of each thread stay in registers between the passes (rows of up to
+// 256 * 8 * KEEP values are read once); chunks beyond them are read again, from L2.
+constexpr int kNormKeep = 8;
+
+__global__ __launch_bounds__(256) void k_rmsnorm_quantize(const uint16_t* __restrict__ x,
+                                                          const uint16_t* __restrict__ gain, float eps,
+                                                          int cols, uint16_t* __restrict__ y,
+                                                          uint8_t* __restrict__ q, float* __restrict__ s) {
+    __shared__ double red[4];
+    const int64_t row = blockIdx.x;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const uint16_t* xr = x + row * cols;
+    const int chunks = cols / 8;
+    const int iters = (chunks + 255) / 256;   // the same for every thread
+    uint4 keep[kNormKeep];
+    double ss = 0.0;
+#pragma unroll
+    for (int i = 0; i < kNormKeep; ++i) {
+        const int c = threadIdx.x + 256 * i;
+        keep[i] = (i < iters && c < chunks) ? *reinterpret_cast<const uint4*>(xr + c * 8) : make_uint4(0, 0, 0, 0);
+    }
+    for (int i = 0; i < iters; ++i) {
+        const int c = threadIdx.x + 256 * i;
+        uint4 raw;
+        if (i < kNormKeep) {
+#pragma unroll
+            for (int k = 0; k < kNormKeep; ++k)
+                if (k == i) raw = keep[k];
+        } else {
+            raw = c < chunks ? *reinterpret_cast<const uint4*>(xr + c * 8) : make_uint4(0, 0, 0, 0);
+        }
+        const uint32_t w4[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const double a = bf16_to_f32(w4[k] & 0xffffu), b = bf16_to_f32(w4[k] >> 16);
+            ss += a * a;
+            ss += b * b;
+        }
+    }
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) ss += __shfl_xor(ss, m);
+    if (lane == 0) red[wave] = ss;
+    __syncthreads();
+    const double total = (red[0] + red[1]) + (red[2] + red[3]);
+    const float var = (float)(total / (double)cols);
+    const float r = (float)(1.0 / sqrt((double)(var + eps)));
+
+    // pass 2; a 16-lane group is one 128-value group, and all 16 lanes of it run every
+    // iteration, so the shuffles inside quant_group stay uniform
+    const int groups = cols / kGroup;
+    const int sub = threadIdx.x & 15;
+    for (int i = 0; i < iters; ++i) {
+        const int c = threadIdx.x + 256 * i;
+        const int g = c >> 4;
+        const bool valid = c < chunks;
+        uint4 raw;
+        if (i < kNormKeep) {
+#pragma unroll
+            for (int k = 0; k < kNormKeep; ++k)
+                if (k == i) raw = keep[k];
+        } else {
+            raw = valid ? *reinterpret_cast<const uint4*>(xr + c * 8) : make_uint4(0, 0, 0, 0);
+        }
+        const uint4 graw = valid ? *reinterpret_cast<const uint4*>(gain + c * 8) : make_uint4(0, 0, 0, 0);
+        const uint32_t xv[4] = {raw.x, raw.y, raw.z, raw.w};
+        const uint32_t gv[4] = {graw.x, graw.y, graw.z, graw.w};
+        uint32_t yv[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const float t0 = bf16_to_f32(f32_to_bf16(bf16_to_f32(xv[k] & 0xffffu) * r));
+            const float t1 = bf16_to_f32(f32_to_bf16(bf16_to_f32(xv[k] >> 16) * r));
+            yv[k] = f32_to_bf16(bf16_to_f32(gv[k] & 0xffffu) * t0) |
+                    (f32_to_bf16(bf16_to_f32(gv[k] >> 16) * t1) << 16);
+        }
+        const uint4 yn = make_uint4(yv[0], yv[1], yv[2], yv[3]);
+        if (valid && y) *reinterpret_cast<uint4*>(y + row * cols + c * 8) = yn;
+        uint2 codes;
+        float sc;
+        quant_group(yn, codes, sc);
+        if (valid) {
+            *reinterpret_cast<uint2*>(q + row * cols + c * 8) = codes;
+            if (sub == 0) s[row * groups + g] = sc;
+        }
+    }
+}
+
+hipError_t launch_rmsnorm_quantize(const uint16_t* x, const uint16_t* gain, float eps, int64_t rows, int cols,
+                                   uint16_t* y, uint8_t* q, float* s, hipStream_t stream) {
+    if (rows == 0) return hipSuccess;
+    if (rows > 0x7fffffff) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(k_rmsnorm_quantize, dim3((unsigned)rows), dim3(256), 0, stream, x, gain, eps, cols, y, q, s);
+    return hipGetLastError();
+}
+
 hipError_t launch_quantize_rows(const uint16_t* x, int64_t rows, int cols, uint8_t* q, float* s,
                                 hipStream_t stream) {
     const int64_t groups = rows * (cols / kGroup);

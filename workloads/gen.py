@@ -33,7 +33,7 @@ GROUP = 128
 FP8_MAX = 448.0
 
 # stream ids for SeedSequence spawning
-_S_X, _S_IDS, _S_W, _S_EXPERTS, _S_SHARED = 1, 2, 3, 4, 5
+_S_X, _S_IDS, _S_W, _S_EXPERTS, _S_SHARED, _S_HIDDEN = 1, 2, 3, 4, 5, 6
 
 
 def _rng(seed: int, stream: int, *extra: int) -> np.random.Generator:
@@ -52,6 +52,17 @@ def make_x_bits(cfg: Config, seed: int | None = None) -> np.ndarray:
     elif cfg.x_mode != "normal":
         raise ValueError(cfg.x_mode)
     return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16).copy()
+
+
+def make_block_inputs(cfg: Config, seed: int | None = None):
+    """Inputs of the FFN half of a block around the layer: the residual stream h[N, d] as
+    bfloat16 bits (float32 N(0,1) rows, not normalised: the block's RMSNorm does that) and
+    the RMSNorm gain [d] as bfloat16 bits (1, the gain the recipe above uses)."""
+    seed = cfg.seed if seed is None else seed
+    h = _rng(seed, _S_HIDDEN).standard_normal((cfg.N, cfg.d), dtype=np.float32)
+    h_bits = torch.from_numpy(h).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16).copy()
+    gain_bits = np.full(cfg.d, 0x3F80, np.uint16)   # bfloat16 1.0
+    return h_bits, gain_bits
 
 
 # --------------------------------------------------------------------------- routing

@@ -117,3 +117,28 @@ def test_profile_api_without_gpu():
     n = ctypes.c_int64()
     assert L.moe_profile_read(99, ctypes.byref(ms), ctypes.byref(n)) == 2
     assert L.moe_profile_read(0, ctypes.byref(ms), ctypes.byref(n)) == 0 and n.value == 0
+
+
+def test_fused_neighbour_calls_validate_on_host():
+    L = _lib.lib()
+    buf = ctypes.create_string_buffer(1 << 16)
+    p = ctypes.cast(buf, ctypes.c_void_p)
+    # RMSNorm + quantisation: cols not a multiple of 128, negative or infinite eps, null, misaligned
+    assert L.moe_rmsnorm_quantize_rows(p, p, 1e-6, 4, 100, NULL, p, p, NULL) == 2
+    assert L.moe_rmsnorm_quantize_rows(p, p, -1.0, 4, 128, NULL, p, p, NULL) == 2
+    assert L.moe_rmsnorm_quantize_rows(p, p, float("inf"), 4, 128, NULL, p, p, NULL) == 2
+    assert L.moe_rmsnorm_quantize_rows(p, p, float("nan"), 4, 128, NULL, p, p, NULL) == 2
+    assert L.moe_rmsnorm_quantize_rows(p, NULL, 1e-6, 4, 128, NULL, p, p, NULL) == 1
+    assert L.moe_rmsnorm_quantize_rows(ctypes.c_void_p(p.value + 2), p, 1e-6, 4, 128, NULL, p, p, NULL) == 3
+    assert L.moe_rmsnorm_quantize_rows(NULL, NULL, 1e-6, 0, 128, NULL, NULL, NULL, NULL) == 0
+    # experts on quantised activations: null scales, misaligned codes, workspace without x_q/x_s
+    args = [p] * 7
+    assert L.moe_grouped_swiglu_q(p, NULL, 4, 2, 8, 128, 128, p, p, *args, p, 1 << 16, 0, NULL) == 1
+    assert L.moe_grouped_swiglu_q(ctypes.c_void_p(p.value + 4), p, 4, 2, 8, 128, 128, p, p, *args, p, 1 << 16, 0,
+                                  NULL) == 3
+    q_ws = L.moe_swiglu_q_workspace_size(4, 2, 8, 128, 128)
+    assert 0 < q_ws < L.moe_swiglu_workspace_size(4, 2, 8, 128, 128)
+    assert L.moe_grouped_swiglu_q(p, p, 4, 2, 8, 128, 128, p, p, *args, p, q_ws - 1, 0, NULL) == 4
+    # combine with the residual: the residual is required
+    assert L.moe_combine_residual(p, p, p, NULL, NULL, 4, 2, 128, p, NULL) == 1
+    assert L.moe_combine_residual(p, p, p, NULL, p, 4, 2, 130, p, NULL) == 2

@@ -160,14 +160,19 @@ def main():
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
+    # an event after every step (recording one does not synchronise) gives per-step times too
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     start.record()
-    for _ in range(args.steps):
+    for i in range(args.steps):
         out = step()
+        marks[i].record()
     end.record()
     torch.cuda.synchronize()
     moe.profile_enable(False)
     total_ms = start.elapsed_time(end)
     ms_per_step = total_ms / args.steps
+    per_step = sorted([start.elapsed_time(marks[0])] +
+                      [marks[i - 1].elapsed_time(marks[i]) for i in range(1, args.steps)])
 
     graph_result = None
     if args.graph:
@@ -239,6 +244,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 4),
+        "step_ms": {"median": round(per_step[len(per_step) // 2], 4), "min": round(per_step[0], 4),
+                    "max": round(per_step[-1], 4)},
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

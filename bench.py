@@ -46,7 +46,7 @@ def parse():
     ap.add_argument("--cpu-tokens", type=int, default=None,
                     help="rows of x in the oracle's CPU-baseline sample (default: whole batch up to 2048 / top_k)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--tile", choices=["auto", "16", "128", "192", "256"], default="auto",
+    ap.add_argument("--tile", choices=["auto", "16", "128", "192", "224", "256"], default="auto",
                     help="force the grouped GEMMs' tile height (default: chosen from rows per expert)")
     ap.add_argument("--block", action="store_true",
                     help="time the FFN half of a block around the layer instead: hidden + layer(RMSNorm(hidden)), "
@@ -137,7 +137,7 @@ def main():
     torch.cuda.synchronize()
 
     flags = {"auto": 0, "16": moe.FLAG_TILE_16, "128": moe.FLAG_TILE_128, "192": moe.FLAG_TILE_192,
-             "256": moe.FLAG_TILE_256}[args.tile]
+             "224": moe.FLAG_TILE_224, "256": moe.FLAG_TILE_256}[args.tile]
 
     if args.block:
         from workloads.gen import make_block_inputs

@@ -77,6 +77,7 @@ typedef enum {
 #define MOE_FLAG_TILE_128 (2u << 4)
 #define MOE_FLAG_TILE_192 (3u << 4)
 #define MOE_FLAG_TILE_256 (4u << 4)
+#define MOE_FLAG_TILE_224 (5u << 4)
 #define MOE_FLAG_TILE_MASK (7u << 4)
 
 /* Limits (checked, MOE_ERR_SHAPE beyond them). */

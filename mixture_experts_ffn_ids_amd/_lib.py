@@ -21,6 +21,7 @@ FLAG_TILE_16 = 1 << 4
 FLAG_TILE_128 = 2 << 4
 FLAG_TILE_192 = 3 << 4
 FLAG_TILE_256 = 4 << 4
+FLAG_TILE_224 = 5 << 4
 
 KERNEL_QUANT, KERNEL_DISPATCH, KERNEL_GATE_UP, KERNEL_DOWN, KERNEL_COMBINE = range(5)
 

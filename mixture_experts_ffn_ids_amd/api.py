@@ -19,7 +19,7 @@ from dataclasses import dataclass
 
 import torch
 
-from ._lib import (FLAG_CHECKED, FLAG_TILE_16, FLAG_TILE_128, FLAG_TILE_192, FLAG_TILE_256,  # noqa: F401
+from ._lib import (FLAG_CHECKED, FLAG_TILE_16, FLAG_TILE_128, FLAG_TILE_192, FLAG_TILE_224, FLAG_TILE_256,  # noqa: F401
                    KERNEL_COMBINE, KERNEL_DISPATCH, KERNEL_DOWN, KERNEL_GATE_UP, KERNEL_QUANT, check, lib)
 
 

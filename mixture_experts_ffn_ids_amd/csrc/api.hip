@@ -154,6 +154,7 @@ TileShape choose_shape(int64_t N, int64_t rows, int32_t E, int32_t d, int32_t d_
         case MOE_FLAG_TILE_16: return TileShape::Rows16;
         case MOE_FLAG_TILE_128: return TileShape::Rows128;
         case MOE_FLAG_TILE_192: return TileShape::Rows192;
+        case MOE_FLAG_TILE_224: return TileShape::Rows224;
         case MOE_FLAG_TILE_256: return TileShape::Rows256;
         default: break;
     }
@@ -161,10 +162,11 @@ TileShape choose_shape(int64_t N, int64_t rows, int32_t E, int32_t d, int32_t d_
     const int64_t per = touched > 0 ? rows / touched : 0;  // expected rows per touched expert
     if (per < 24) return TileShape::Rows16;
     if (per < 112) return TileShape::Rows128;
-    // 256-row tiles only where one of them holds an expert's rows that would need two
-    // 192-row tiles; experts with more rows than that run faster in 192-row tiles, whose
-    // deeper weight ring fits in LDS
-    if (per < 184 || per > 256) return TileShape::Rows192;
+    // a 224- or 256-row tile where one tile holds nearly every expert's rows (expert counts
+    // spread around their mean); experts with many more rows run faster in 192-row tiles,
+    // and 256-row tiles keep only a 2-stage weight ring
+    if (per < 150 || per > 256) return TileShape::Rows192;
+    if (per < 200) return TileShape::Rows224;
     return TileShape::Rows256;
 }
 

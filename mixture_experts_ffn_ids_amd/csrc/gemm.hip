@@ -294,6 +294,7 @@ int tile_rows(TileShape shape) {
         case TileShape::Rows16: return 16;
         case TileShape::Rows128: return 128;
         case TileShape::Rows192: return 192;
+        case TileShape::Rows224: return 224;
         default: return 256;
     }
 }

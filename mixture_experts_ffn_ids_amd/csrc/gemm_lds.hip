@@ -10,7 +10,7 @@
 // fp32 accumulator.
 //
 // Workgroup: 8 waves (2 along the rows x 4 along the weight rows), 512 threads. It owns
-// one tile (<= BM = 32 MT sorted rows of one expert, MT = 4, 6 or 8) and 256 weight rows:
+// one tile (<= BM = 32 MT sorted rows of one expert, MT = 4, 6, 7 or 8) and 256 weight rows:
 // for gate|up the 128 gate and 128 up rows of one 128-wide d_ff block (so the
 // requantisation group is complete), for down 256 output columns. Each wave computes
 // 16 MT rows x 4 weight-row subtiles of 16 (64 columns): MT x 4 MFMA tiles.
@@ -70,7 +70,7 @@ struct Cfg {
     static constexpr int A_BYTES = BM * 128;      // one activation stage
     static constexpr int B_BYTES = BR * 128;      // one weight stage
     static constexpr int NA = BM <= 128 ? 3 : 2;  // activation stages
-    static constexpr int NBS = BM <= 192 ? 3 : 2; // weight stages
+    static constexpr int NBS = BM <= 224 ? 3 : 2; // weight stages
     // waves 0..3 copy the activations and their row scales, waves 4..7 the weights, so that
     // each wave's in-order copy counter tracks one ring only
     static constexpr int ROLE_W = NW / 2;
@@ -86,7 +86,7 @@ struct Cfg {
     //      [BM] | weight block scales [2][MAX_KB]
     static constexpr int LDS = MAIN + NA * S_STAGE * 4 + BM * 4 + 2 * MAX_KB * 4;
     static_assert(A_Q * ROLE_W * 64 == BM * 8 && B_Q * ROLE_W * 64 == BR * 8, "copy split");
-    static_assert(S_L <= 64 && BM % ROLE_W == 0 && MT % 2 == 0, "scale copies");
+    static_assert(S_L <= 64 && BM % ROLE_W == 0, "scale copies");
     static_assert(LDS <= 160 * 1024, "LDS budget");
     static_assert(A_Q + 1 <= 15 && B_Q <= 15, "pending copies fit the wait helper");
 };
@@ -332,11 +332,16 @@ __global__ __launch_bounds__(512) void k_gemm_lds(const LdsGemmParams P) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) bf[j] = lds_frag(B, bbase[j] + rlane, kg);
             float sa[MT];
+            if constexpr (MT % 2 == 0) {   // pairs are 8-byte aligned when MT is even
 #pragma unroll
-            for (int mt = 0; mt < MT; mt += 2) {
-                const float2 v = *reinterpret_cast<const float2*>(SA + mt);
-                sa[mt] = v.x;
-                sa[mt + 1] = v.y;
+                for (int mt = 0; mt < MT; mt += 2) {
+                    const float2 v = *reinterpret_cast<const float2*>(SA + mt);
+                    sa[mt] = v.x;
+                    sa[mt + 1] = v.y;
+                }
+            } else {
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) sa[mt] = SA[mt];
             }
             // one row subtile at a time (a scheduling barrier after each keeps the compiler
             // from gathering all of them, which would hold every fragment at once); the next
@@ -566,6 +571,7 @@ hipError_t launch_gate_up_lds(const GateUpArgs& a, int rows, hipStream_t stream)
     switch (rows) {
         case 128: return launch_lds<0, 4>(P, a.max_tiles, stream);
         case 192: return launch_lds<0, 6>(P, a.max_tiles, stream);
+        case 224: return launch_lds<0, 7>(P, a.max_tiles, stream);
         default: return launch_lds<0, 8>(P, a.max_tiles, stream);
     }
 }
@@ -580,6 +586,7 @@ hipError_t launch_down_lds(const DownArgs& a, int rows, hipStream_t stream) {
     switch (rows) {
         case 128: return launch_lds<1, 4>(P, a.max_tiles, stream);
         case 192: return launch_lds<1, 6>(P, a.max_tiles, stream);
+        case 224: return launch_lds<1, 7>(P, a.max_tiles, stream);
         default: return launch_lds<1, 8>(P, a.max_tiles, stream);
     }
 }

@@ -68,8 +68,6 @@ __device__ __forceinline__ v4f mfma_16x16x128_fp8(const v8i& a, const v8i& b) {
 }
 
 // ---------------------------------------------------------------- launchers
-struct GemmPlan;
-
 hipError_t launch_quantize_rows(const uint16_t* x, int64_t rows, int cols, uint8_t* q, float* s,
                                 hipStream_t stream);
 hipError_t launch_rmsnorm_quantize(const uint16_t* x, const uint16_t* gain, float eps, int64_t rows, int cols,
@@ -97,7 +95,7 @@ int64_t max_tiles(int64_t rows, int E, int BM);
 hipError_t launch_build_tiles(const int32_t* offsets, int E, int64_t rows, int BM, int64_t max_tiles,
                               Tile* tiles, int32_t* num_tiles, hipStream_t stream);
 
-enum class TileShape { Rows16 = 0, Rows128 = 1, Rows192 = 2, Rows256 = 3 };
+enum class TileShape { Rows16 = 0, Rows128 = 1, Rows192 = 2, Rows224 = 3, Rows256 = 4 };
 int tile_rows(TileShape shape);   // BM of the gate|up and down kernels for this shape
 
 struct GateUpArgs {
@@ -127,7 +125,7 @@ struct DownArgs {
 hipError_t launch_gate_up(const GateUpArgs& a, TileShape shape, hipStream_t stream);
 hipError_t launch_down(const DownArgs& a, TileShape shape, hipStream_t stream);
 
-// LDS-staged kernels for tiles of 128, 192 or 256 rows (gemm_lds.hip)
+// LDS-staged kernels for tiles of 128, 192, 224 or 256 rows (gemm_lds.hip)
 hipError_t launch_gate_up_lds(const GateUpArgs& a, int rows, hipStream_t stream);
 hipError_t launch_down_lds(const DownArgs& a, int rows, hipStream_t stream);
 

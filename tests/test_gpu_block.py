@@ -48,8 +48,8 @@ def test_rmsnorm_quantize_bit_exact(rows, cols):
     assert y2 is None and torch.equal(q2, q) and torch.equal(s2, s)
 
 
-@pytest.mark.parametrize("flags", [0, moe.FLAG_TILE_16, moe.FLAG_TILE_128, moe.FLAG_TILE_192, moe.FLAG_TILE_256],
-                         ids=["auto", "16", "128", "192", "256"])
+@pytest.mark.parametrize("flags", [0, moe.FLAG_TILE_16, moe.FLAG_TILE_128, moe.FLAG_TILE_192, moe.FLAG_TILE_224,
+                                   moe.FLAG_TILE_256], ids=["auto", "16", "128", "192", "224", "256"])
 def test_grouped_swiglu_on_quantised_input_matches(flags):
     cfg = Config("q_in", 200, 384, 256, 5, 2, "normal", "uniform", "softmax", False, seed=51)
     from workloads import make_x_bits

@@ -16,8 +16,8 @@ pytestmark = pytest.mark.gpu
 CFG = Config("graph", 300, 256, 256, 4, 2, "normal", "uniform", "softmax", True, seed=21)
 
 
-@pytest.mark.parametrize("flags", [0, moe.FLAG_TILE_16, moe.FLAG_TILE_128, moe.FLAG_TILE_192],
-                         ids=["auto", "16", "128", "192"])
+@pytest.mark.parametrize("flags", [0, moe.FLAG_TILE_16, moe.FLAG_TILE_128, moe.FLAG_TILE_192, moe.FLAG_TILE_224],
+                         ids=["auto", "16", "128", "192", "224"])
 def test_layer_replays_in_a_hip_graph(flags):
     x_bits = make_x_bits(CFG)
     x2_bits = make_x_bits(CFG, seed=22)

@@ -14,7 +14,8 @@ from workloads.gen import HostExperts, experts_to_host, make_experts_device, mak
 
 pytestmark = pytest.mark.gpu
 
-SHAPES = {"16": moe.FLAG_TILE_16, "128": moe.FLAG_TILE_128, "192": moe.FLAG_TILE_192, "256": moe.FLAG_TILE_256}
+SHAPES = {"16": moe.FLAG_TILE_16, "128": moe.FLAG_TILE_128, "192": moe.FLAG_TILE_192, "224": moe.FLAG_TILE_224,
+          "256": moe.FLAG_TILE_256}
 
 
 def _layer(x_bits, ids, w, ex_dev, sh_dev=None, flags=0):
@@ -26,7 +27,7 @@ def _layer(x_bits, ids, w, ex_dev, sh_dev=None, flags=0):
     return bits_host(out)
 
 
-def _check_small(cfg: Config, ids=None, w=None, shapes=("auto", "16", "128", "192", "256")):
+def _check_small(cfg: Config, ids=None, w=None, shapes=("auto", "16", "128", "192", "224", "256")):
     x = make_x_bits(cfg)
     if ids is None:
         ids, w = make_routing(cfg)

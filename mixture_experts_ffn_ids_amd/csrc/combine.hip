@@ -20,6 +20,14 @@ __device__ __forceinline__ void unpack8(const uint4 r, float (&f)[8]) {
     f[6] = bf16_to_f32(r.w & 0xffffu); f[7] = bf16_to_f32(r.w >> 16);
 }
 
+// Expert outputs are read exactly once: their loads carry the nontemporal hint, which
+// measured 12% faster at prefill (940 MB of y_sorted) than plain loads.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 load_once(const uint4* p) {
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 // One wave per (token, 1024-column slice); lane L owns 16-B chunks L and L + 64 of the
 // slice. The token's K source rows and weights are read once (lanes < K) and broadcast by
 // lane reads; for each batch of up to 8 choices every load of both chunks is issued before
@@ -59,8 +67,8 @@ __global__ __launch_bounds__(256) void k_combine(const uint16_t* __restrict__ y,
             pk[kk] = __shfl(my_p, k);
             const bool ok = k0 + kk < K && pk[kk] >= 0;
             const uint4* src = reinterpret_cast<const uint4*>(y + (int64_t)(ok ? pk[kk] : 0) * d) + c0;
-            r[kk][0] = (ok && v0) ? src[0] : make_uint4(0, 0, 0, 0);
-            r[kk][1] = (ok && v1) ? src[64] : make_uint4(0, 0, 0, 0);
+            r[kk][0] = (ok && v0) ? load_once(src) : make_uint4(0, 0, 0, 0);
+            r[kk][1] = (ok && v1) ? load_once(src + 64) : make_uint4(0, 0, 0, 0);
         }
 #pragma unroll
         for (int kk = 0; kk < 8; ++kk) {

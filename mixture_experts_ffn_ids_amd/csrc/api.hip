@@ -133,7 +133,7 @@ SwigluWs swiglu_layout(int64_t N, int32_t K, int32_t E, int32_t d, int32_t d_ff,
     // sized for the smallest tile height, so every tile shape fits
     w.tile_cap = max_tiles(rows, E, tile_rows(TileShape::Rows16));
     w.tiles = off; off = align_up(off + (size_t)w.tile_cap * sizeof(Tile));
-    w.ntiles = off; off = align_up(off + sizeof(int32_t));
+    w.ntiles = off; off = align_up(off + 2 * sizeof(int32_t));   // tile count, one-tile-per-expert flag
     w.total = off;
     return w;
 }

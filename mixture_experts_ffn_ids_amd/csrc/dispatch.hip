@@ -168,6 +168,7 @@ int64_t max_tiles(int64_t rows, int E, int BM) {
     return rows / BM + nonempty + 1;
 }
 
+// num_tiles[0]: tiles written; num_tiles[1]: 1 when every expert with rows got one tile
 __global__ __launch_bounds__(1024) void k_tiles(const int32_t* __restrict__ offsets, int E, int64_t rows,
                                                 int BM, int64_t cap, Tile* __restrict__ tiles,
                                                 int32_t* __restrict__ num_tiles) {
@@ -175,14 +176,16 @@ __global__ __launch_bounds__(1024) void k_tiles(const int32_t* __restrict__ offs
     // so that any offsets array yields in-bounds tiles
     const int per = (E + blockDim.x - 1) / blockDim.x;
     const int e0 = threadIdx.x * per;
-    int64_t local = 0;
+    int64_t local = 0, local_busy = 0;
     for (int e = e0; e < e0 + per && e < E; ++e) {
         int64_t b = offsets[e], en = offsets[e + 1];
         b = b < 0 ? 0 : (b > rows ? rows : b);
         en = en < b ? b : (en > rows ? rows : en);
         local += (en - b + BM - 1) / BM;
+        local_busy += en > b ? 1 : 0;
     }
-    int64_t total;
+    int64_t total, busy;
+    block_exclusive_scan<int64_t>(local_busy, &busy);
     int64_t t = block_exclusive_scan<int64_t>(local, &total);
     for (int e = e0; e < e0 + per && e < E; ++e) {
         int64_t b = offsets[e], en = offsets[e + 1];
@@ -202,7 +205,12 @@ __global__ __launch_bounds__(1024) void k_tiles(const int32_t* __restrict__ offs
             tiles[t] = tl;
         }
     }
-    if (threadIdx.x == 0) *num_tiles = (int32_t)(total < cap ? total : cap);
+    if (threadIdx.x == 0) {
+        num_tiles[0] = (int32_t)(total < cap ? total : cap);
+        // every expert with rows fits one tile: each weight block is then read by one
+        // workgroup only
+        num_tiles[1] = total == busy && total <= cap ? 1 : 0;
+    }
 }
 
 hipError_t launch_build_tiles(const int32_t* offsets, int E, int64_t rows, int BM, int64_t cap, Tile* tiles,

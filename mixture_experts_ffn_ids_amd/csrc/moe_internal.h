@@ -92,6 +92,7 @@ struct Tile {
 
 int64_t max_tiles(int64_t rows, int E, int BM);
 
+// num_tiles[2]: the number of tiles, and 1 if every expert with rows got exactly one tile
 hipError_t launch_build_tiles(const int32_t* offsets, int E, int64_t rows, int BM, int64_t max_tiles,
                               Tile* tiles, int32_t* num_tiles, hipStream_t stream);
 

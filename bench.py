@@ -18,6 +18,9 @@ quantised product it writes.
 The CPU baseline is the plain oracle (test infrastructure) on a bounded sample of
 the same batch, on this host's cores.
 
+For the dense workload (the dense block's SwiGLU MLP) a step is that MLP over the batch, run
+through the same kernels as one expert that every token visits (dense_swiglu).
+
 With --graph the step is also captured once in a HIP graph and replayed; its time is
 reported under "graph" (the headline value and the kernel timings stay eager).
 """
@@ -44,7 +47,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="k2_decode_256")
     ap.add_argument("--cpu-tokens", type=int, default=None,
-                    help="rows of x in the oracle's CPU-baseline sample (default: whole batch up to 2048 / top_k)")
+                    help="rows of x in the oracle's CPU-baseline sample (default: whole batch up to "
+                         "2048 * 2048 / (top_k * d_ff))")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--tile", choices=["auto", "16", "128", "192", "224", "256"], default="auto",
                     help="force the grouped GEMMs' tile height (default: chosen from rows per expert)")
@@ -145,8 +149,15 @@ def main():
         hidden = torch.from_numpy(h_bits.view(np.int16)).view(torch.bfloat16).to(dev)
         gain = torch.from_numpy(g_bits.view(np.int16)).view(torch.bfloat16).to(dev)
 
+        if cfg.dense:
+            def step():
+                return moe.dense_block_ffn(hidden, gain, 1e-6, experts, flags=flags)
+        else:
+            def step():
+                return moe.moe_block_ffn(hidden, gain, 1e-6, t_ids, t_w, experts, shared, flags=flags)
+    elif cfg.dense:
         def step():
-            return moe.moe_block_ffn(hidden, gain, 1e-6, t_ids, t_w, experts, shared, flags=flags)
+            return moe.dense_swiglu(x, experts, flags=flags)
     else:
         def step():
             return moe.moe_layer(x, t_ids, t_w, experts, shared, flags=flags)
@@ -273,6 +284,11 @@ def main():
         result["config"]["block"] = ("hidden + layer(RMSNorm(hidden)): the block's RMSNorm fused into the "
                                      "activation quantisation (kernel 'quant'), its residual addition into "
                                      "the combine")
+    if cfg.dense:
+        result["config"]["dense"] = (f"the dense block's SwiGLU MLP (intermediate size {d_ff}, an assumption: the "
+                                     f"pages print none) run as one expert that every token visits; no routing "
+                                     f"weights, no combine" + ("" if not args.block else " beyond the residual "
+                                                               "addition"))
     if cfg.shard_topk:
         result["config"]["shard"] = (f"one GPU's part of an expert-parallel layer: {N} received rows (token "
                                      f"choices of a top-{cfg.shard_topk} router) over its {E} local experts, "
@@ -282,7 +298,8 @@ def main():
     if not args.no_cpu_baseline:
         import oracle
         from workloads.gen import experts_to_host
-        n_cpu = args.cpu_tokens or min(N, 2048 // K)   # about 2048 expert evaluations per pass
+        # about 2048 evaluations of a 2048-wide expert per pass
+        n_cpu = args.cpu_tokens or max(1, min(N, 2048 * 2048 // (K * d_ff)))
         tok = np.arange(n_cpu, dtype=np.int64)
         exh = experts_to_host(experts, np.unique(ids[tok]))
         shh = experts_to_host(shared) if shared is not None else None

@@ -248,6 +248,49 @@ def moe_block_ffn(hidden: torch.Tensor, gain: torch.Tensor, eps: float, topk_ids
     return combine(y, disp, topk_w, shared, out=out, residual=hidden)
 
 
+# ---------------------------------------------------------------- dense block
+_ONES: dict = {}
+
+
+def _unit_weights(N: int, dev: torch.device) -> torch.Tensor:
+    """[N, 1] float32 ones, cached per device (a larger cached column is sliced; an outgrown
+    one stays allocated, as a captured graph may address it)."""
+    key = str(dev)
+    t = _ONES.get(key)
+    if t is None or t.shape[0] < N:
+        if t is not None:
+            _WS_RETIRED.append(t)
+        t = torch.ones((max(N, 1), 1), dtype=torch.float32, device=dev)
+        _ONES[key] = t
+    return t[:N]
+
+
+def dense_swiglu(x: torch.Tensor, mlp, flags: int = 0, out: torch.Tensor | None = None) -> torch.Tensor:
+    """The dense block's SwiGLU MLP, down(silu(gate x) * up x), through the grouped kernels
+    as one expert that every token visits (E = 1, K = 1): out [N, d] bf16 in token order.
+    mlp holds the three projections like an expert set with E = 1; the intermediate size is
+    whatever its weights have (any multiple of 128)."""
+    _want(x, torch.bfloat16, "x", 2)
+    if mlp.w_gate.shape[0] != 1:
+        raise ValueError("a dense MLP is an expert set with E = 1")
+    return grouped_swiglu(x, identity_dispatch(x.shape[0], x.device), mlp, flags, out)
+
+
+def dense_block_ffn(hidden: torch.Tensor, gain: torch.Tensor, eps: float, mlp, flags: int = 0,
+                    out: torch.Tensor | None = None) -> torch.Tensor:
+    """The FFN half of a dense block: hidden + MLP(RMSNorm(hidden)), with the RMSNorm fused
+    into the activation quantisation and the residual addition done by the combine (one
+    choice of weight 1 per token). out may be hidden itself."""
+    _want(hidden, torch.bfloat16, "hidden", 2)
+    if mlp.w_gate.shape[0] != 1:
+        raise ValueError("a dense MLP is an expert set with E = 1")
+    N = hidden.shape[0]
+    xq, xs, _ = rmsnorm_quantize(hidden, gain, eps)
+    disp = identity_dispatch(N, hidden.device)
+    y = grouped_swiglu_q(xq, xs, disp, mlp, flags)
+    return combine(y, disp, _unit_weights(N, hidden.device), out=out, residual=hidden)
+
+
 # ---------------------------------------------------------------- profiling
 def profile_enable(on: bool = True):
     check(lib().moe_profile_enable(1 if on else 0), "moe_profile_enable")

@@ -20,6 +20,13 @@ contributes two rows, and whether those rows hold equal values changes no work.
 The layer call on such a shard (K = 1, unit weights) is the receiving rank's whole
 part: sort the rows by local expert, run the experts, and put the outputs back in
 arrival order (the combine of one unit-weight choice is that inverse permutation).
+
+The seventh workload is the dense block's SwiGLU MLP ("SwiGLU output" page: one dense
+block whose feed-forward network is the same down(silu(gate x) * up x) with the model's
+intermediate_size) at 8192 tokens: one expert that every token visits with weight 1.
+The pages print no value for that intermediate size. The workload takes 18432 (9 x 2048,
+the size of the public configs of this architecture family, an assumption); the kernels
+take any multiple of 128.
 """
 from __future__ import annotations
 
@@ -44,6 +51,8 @@ class Config:
     # > 0: the workload is one GPU's shard of an expert-parallel layer whose router picks
     # this many experts per token; its N rows are received token choices, E the local experts
     shard_topk: int = 0
+    # the dense block's MLP (E = 1, K = 1, unit weights) rather than a routed layer
+    dense: bool = False
 
     @property
     def slots(self) -> int:
@@ -62,6 +71,7 @@ CONFIGS = [
     Config("k2_prefill_8192", 8192, 7168, 2048, 384, 8, "rmsnorm", "uniform", "uniform", False),
     Config("k2_skewed_shared_4096", 4096, 7168, 2048, 384, 8, "rmsnorm", "zipf", "dirichlet", True),
     Config("k2_ep8_shard_8192", 65536, 7168, 2048, 48, 1, "rmsnorm", "uniform", "ones", False, shard_topk=8),
+    Config("k2_dense_8192", 8192, 7168, 18432, 1, 1, "rmsnorm", "uniform", "ones", False, dense=True),
 ]
 
 

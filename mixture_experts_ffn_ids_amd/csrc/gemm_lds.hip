@@ -27,10 +27,11 @@
 // wait for older weight copies (from HBM) before its newer activation copies (from L2)
 // counted as landed.
 //   * weights (256 x 128 B) into a ring of 3 stages (2 for 256-row tiles, where LDS runs
-//     out), so that two weight blocks are in flight from HBM while one is multiplied;
+//     out), so that two weight blocks are in flight from HBM while one is multiplied. The
+//     kernel waits on these copies' latency: a ring of 2 instead of 3 costs 30%;
 //   * activations (BM x 128 B, gathered token rows for gate|up) and their row scales into
-//     a ring of 3 stages for 128-row tiles and 2 otherwise (they come mostly from L2: the
-//     16 n-blocks of a tile run together on one XCD).
+//     a ring of 2 stages (they come mostly from L2: the n-blocks of a tile run together on
+//     one XCD; a third stage measured 3-5% slower at 128 rows).
 // Rows are 128 B with 16-B chunks XOR-swizzled so that fragment reads are free of bank
 // conflicts. Row scales are stored so that the MT scales one lane needs are adjacent.
 // Rows past the end of the tile copy a valid row (the tile's first row, or the last weight
@@ -69,7 +70,7 @@ struct Cfg {
     static constexpr int BR = 256;                // weight rows per workgroup
     static constexpr int A_BYTES = BM * 128;      // one activation stage
     static constexpr int B_BYTES = BR * 128;      // one weight stage
-    static constexpr int NA = BM <= 128 ? 3 : 2;  // activation stages
+    static constexpr int NA = 2;                  // activation stages
     static constexpr int NBS = BM <= 224 ? 3 : 2; // weight stages
     // waves 0..3 copy the activations and their row scales, waves 4..7 the weights, so that
     // each wave's in-order copy counter tracks one ring only
@@ -88,7 +89,8 @@ struct Cfg {
     static_assert(A_Q * ROLE_W * 64 == BM * 8 && B_Q * ROLE_W * 64 == BR * 8, "copy split");
     static_assert(S_L <= 64 && BM % ROLE_W == 0, "scale copies");
     static_assert(LDS <= 160 * 1024, "LDS budget");
-    static_assert(A_Q + 1 <= 15 && B_Q <= 15, "pending copies fit the wait helper");
+    static_assert(NA >= 2 && NA <= 4 && NBS >= 2 && NBS <= 4, "ring depths");
+    static_assert((NA - 2) * (A_Q + 1) <= 63 && (NBS - 2) * B_Q <= 63, "pending copies fit the wait counter");
 };
 
 struct LdsGemmParams {
@@ -156,27 +158,6 @@ __device__ __forceinline__ void copy4(const void* g, uint32_t off, uint32_t l) {
 template <int N>
 __device__ __forceinline__ void wait_copies() {
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-// the same with N known only at run time (uniform over the wave; at most 15 here)
-__device__ __forceinline__ void wait_pending(int n) {
-    switch (n) {
-        case 0: wait_copies<0>(); break;
-        case 1: wait_copies<1>(); break;
-        case 2: wait_copies<2>(); break;
-        case 3: wait_copies<3>(); break;
-        case 4: wait_copies<4>(); break;
-        case 5: wait_copies<5>(); break;
-        case 6: wait_copies<6>(); break;
-        case 7: wait_copies<7>(); break;
-        case 8: wait_copies<8>(); break;
-        case 9: wait_copies<9>(); break;
-        case 10: wait_copies<10>(); break;
-        case 11: wait_copies<11>(); break;
-        case 12: wait_copies<12>(); break;
-        case 13: wait_copies<13>(); break;
-        case 14: wait_copies<14>(); break;
-        default: wait_copies<15>(); break;
-    }
 }
 
 // Row of the tile whose activation scale sits in slot `slot` of a row-scale stage: the MT
@@ -336,7 +317,7 @@ __global__ __launch_bounds__(512) void k_gemm_lds(const LdsGemmParams P) {
         // matrix work instead of preceding it
         // Exception: with a 2-stage activation ring an A-wave issues its whole block first,
         // for the most lead time (its copies must land by the end of this iteration).
-        constexpr int SLOTS = (BW || NA == 3) ? MT : 1;
+        constexpr int SLOTS = (BW || NA > 2) ? MT : 1;
         auto compute = [&](int kb, auto issue_tag, int next) {
             constexpr bool ISSUE = decltype(issue_tag)::value;
             const uint8_t* A = sA + (kb % NA) * C::A_BYTES;
@@ -399,10 +380,15 @@ __global__ __launch_bounds__(512) void k_gemm_lds(const LdsGemmParams P) {
         // at once; meanwhile the A-waves (no copies in flight yet, so their loads cost no
         // extra waits) fill the tables of source rows and weight block scales, and after the
         // barrier that publishes them they issue the activations' first blocks.
+        // the first NR - 1 blocks of a role's ring (fewer when K is shorter)
+        auto prologue = [&]() {
+#pragma unroll
+            for (int b = 0; b < NR - 1; ++b)
+                if (b < KB) issue(b, 0, NQ);
+        };
         if constexpr (BW) {
             plan();
-            issue(0, 0, NQ);
-            if (NR == 3 && KB > 1) issue(1, 0, NQ);
+            prologue();
         } else {
             // source row of every tile row; rows past the end repeat the tile's first row
             for (int r = tid; r < BM; r += C::ROLE_W * 64) {
@@ -435,21 +421,24 @@ __global__ __launch_bounds__(512) void k_gemm_lds(const LdsGemmParams P) {
         __syncthreads();
         if constexpr (!BW) {
             plan();
-            issue(0, 0, NQ);
-            if (NR == 3 && KB > 1) issue(1, 0, NQ);
+            prologue();
         }
-        wait_pending(NR == 3 && KB > 1 ? NQ : 0);
+        // block 0 landed; the later prologue blocks may still be in flight
+        if (KB >= NR - 1)
+            wait_copies<(NR - 2) * NQ>();
+        else
+            wait_copies<0>();
         __syncthreads();
 
         // steady state: every ring is refilled in every iteration and the wait count is a
         // constant, with no branch between the matrix work and the wait
         constexpr int AHEAD = (NA > NBS ? NA : NBS) - 1;
-        static_assert(AHEAD == 1 || AHEAD == 2, "ring depths of 2 or 3");
+        static_assert(AHEAD >= 1 && AHEAD <= 3, "ring depths of 2 to 4");
         for (int kb = 0; kb < KB - AHEAD; ++kb) {
             // refill the stage read in iteration kb - 1 (the barrier below separates them)
             compute(kb, std::true_type{}, kb + NR - 1);
             __builtin_amdgcn_sched_barrier(0);
-            wait_copies<NR == 3 ? NQ : 0>();
+            wait_copies<(NR - 2) * NQ>();
             __syncthreads();
         }
         // the last AHEAD blocks (t = 0 .. AHEAD-1 is block KB - AHEAD + t, skipped when K is
@@ -465,6 +454,7 @@ __global__ __launch_bounds__(512) void k_gemm_lds(const LdsGemmParams P) {
         };
         drain(std::integral_constant<int, 0>{});
         if constexpr (AHEAD > 1) drain(std::integral_constant<int, 1>{});
+        if constexpr (AHEAD > 2) drain(std::integral_constant<int, 2>{});
     };
     // every variant passes the same barriers, so the waves of one workgroup may differ.
     // Only gate|up has the streaming variant: down gained nothing from it, and its extra

@@ -165,6 +165,33 @@ moe_status moe_grouped_swiglu_q(const uint8_t* xq, const float* xs, int64_t N, i
                                 void* stream);
 
 /* ------------------------------------------------------------------------
+ * Grouped SwiGLU experts of a top-1 dispatch (K = 1) with the weighted
+ * combine done by the down projection's epilogue ("Mixture of experts" page,
+ * Code: moe_infer's weighted sum, which for one choice per token is a scaled
+ * copy back to token order; the same page's moe-init evidence: a GPU of an
+ * expert-parallel group runs its local experts on rows it received, one
+ * choice per row, and returns them in arrival order):
+ *   out[n] = bfloat16( 0 + w[n] * y[n] ),  y[n] = the bfloat16 expert output
+ * of token n as moe_grouped_swiglu computes it. The result equals
+ * moe_grouped_swiglu followed by moe_combine (K = 1, no shared expert) bit for
+ * bit, without the y_sorted round trip through memory.
+ * x[N][d] bf16; offsets[E+1] and sorted_slot[N] from moe_dispatch with K = 1;
+ * topk_w[N] float32; weights as moe_grouped_swiglu; out[N][d] bf16, which
+ * must not overlap x. The workspace needs moe_swiglu_workspace_size(N, 1, E,
+ * d, d_ff) bytes. A token whose id moe_dispatch left out (out of range, fast
+ * mode) keeps its previous out row; every other row is written exactly once.
+ * Shapes, alignment and flags as moe_grouped_swiglu. N = 0 is a no-op.
+ * ---------------------------------------------------------------------- */
+moe_status moe_grouped_swiglu_top1(const uint16_t* x, int64_t N, int32_t E, int32_t d,
+                                   int32_t d_ff, const int32_t* offsets,
+                                   const int32_t* sorted_slot, const float* topk_w,
+                                   const uint8_t* w_gate, const float* s_gate,
+                                   const uint8_t* w_up, const float* s_up,
+                                   const uint8_t* w_down, const float* s_down, uint16_t* out,
+                                   void* workspace, size_t workspace_bytes, uint32_t flags,
+                                   void* stream);
+
+/* ------------------------------------------------------------------------
  * Weighted combine ("Mixture of experts" page, Code: moe_infer's weighted sum
  * over the K outputs of each token, and forward's addition of the shared
  * expert):

@@ -168,6 +168,30 @@ def grouped_swiglu_q(xq: torch.Tensor, xs: torch.Tensor, disp: Dispatch, experts
     return out
 
 
+def grouped_swiglu_top1(x: torch.Tensor, disp: Dispatch, topk_w: torch.Tensor, experts, flags: int = 0,
+                        out: torch.Tensor | None = None) -> torch.Tensor:
+    """out [N, d] bf16 = topk_w[n] * expert(x[n]) for a top-1 dispatch (K = 1): the grouped
+    experts with the combine done by the down projection's epilogue. Bit-identical to
+    combine(grouped_swiglu(x, disp, experts), disp, topk_w)."""
+    _want(x, torch.bfloat16, "x", 2)
+    _want(topk_w, torch.float32, "topk_w", 2)
+    N, d = x.shape
+    if disp.K != 1 or tuple(topk_w.shape) != (N, 1):
+        raise ValueError("grouped_swiglu_top1 needs a K = 1 dispatch and topk_w of shape [N, 1]")
+    E, d_ff = _expert_dims(experts, d, N, disp)
+    ex = experts
+    out = _y_out(out, N, d, x.device)
+    if out.data_ptr() == x.data_ptr() and N:
+        raise ValueError("out must not overlap x")
+    nb = lib().moe_swiglu_workspace_size(N, 1, E, d, d_ff)
+    ws = _workspace(nb, x.device, "swiglu")
+    st = lib().moe_grouped_swiglu_top1(_p(x), N, E, d, d_ff, _p(disp.offsets), _p(disp.sorted_slot), _p(topk_w),
+                                       _p(ex.w_gate), _p(ex.s_gate), _p(ex.w_up), _p(ex.s_up), _p(ex.w_down),
+                                       _p(ex.s_down), _p(out), _p(ws), ws.numel(), int(flags), _stream(x.device))
+    check(st, "moe_grouped_swiglu_top1")
+    return out
+
+
 def combine(y_sorted: torch.Tensor, disp: Dispatch, topk_w: torch.Tensor,
             shared: torch.Tensor | None = None, out: torch.Tensor | None = None,
             residual: torch.Tensor | None = None) -> torch.Tensor:
@@ -222,6 +246,9 @@ def moe_layer(x: torch.Tensor, topk_ids: torch.Tensor, topk_w: torch.Tensor, exp
     same shapes, which sizes the cached workspaces."""
     E = experts.w_gate.shape[0]
     disp = dispatch(topk_ids, E)
+    if disp.K == 1 and shared_expert is None:
+        # one choice per token: the combine is done by the down projection's epilogue
+        return grouped_swiglu_top1(x, disp, topk_w, experts, flags)
     y = grouped_swiglu(x, disp, experts, flags)
     shared = None
     if shared_expert is not None:

@@ -244,21 +244,24 @@ size_t moe_swiglu_q_workspace_size(int64_t N, int32_t K, int32_t E, int32_t d, i
 
 namespace {
 
-// Shared by moe_grouped_swiglu (with_x: x is the bf16 input, quantised into the workspace)
-// and moe_grouped_swiglu_q (xq_in and xs_in are given).
+// Shared by moe_grouped_swiglu (with_x: x is the bf16 input, quantised into the workspace),
+// moe_grouped_swiglu_q (xq_in and xs_in are given) and moe_grouped_swiglu_top1 (top1_w
+// given, K = 1: y_sorted is then the token-order output, written by the down epilogue).
 moe_status grouped_swiglu(bool with_x, const uint16_t* x, const uint8_t* xq_in, const float* xs_in, int64_t N,
                           int32_t K, int32_t E, int32_t d, int32_t d_ff, const int32_t* offsets,
                           const int32_t* sorted_slot,
                           const uint8_t* w_gate, const float* s_gate, const uint8_t* w_up, const float* s_up,
                           const uint8_t* w_down, const float* s_down, uint16_t* y_sorted, void* workspace,
-                          size_t workspace_bytes, uint32_t flags, void* stream) {
+                          size_t workspace_bytes, uint32_t flags, void* stream, const float* top1_w = nullptr,
+                          bool top1 = false) {
     if (N < 0 || K < 1 || E < 1 || E > MOE_MAX_EXPERTS || K > MOE_MAX_TOPK || K > E || !dim_ok(d) ||
         !dim_ok(d_ff) || N * (int64_t)K > 0x7fffffffLL)
         return MOE_ERR_SHAPE;
     if (N == 0) return MOE_OK;
     if ((with_x ? !x : (!xq_in || !xs_in)) || !offsets || !sorted_slot || !w_gate || !s_gate || !w_up || !s_up ||
-        !w_down || !s_down || !y_sorted || !workspace)
+        !w_down || !s_down || !y_sorted || !workspace || (top1 && !top1_w))
         return MOE_ERR_NULL;
+    if (top1 && !aligned(top1_w, 4)) return MOE_ERR_ALIGN;
     if ((with_x ? !aligned(x, 16) : (!aligned(xq_in, 16) || !aligned(xs_in, 4))) || !aligned(w_gate, 16) ||
         !aligned(w_up, 16) || !aligned(w_down, 16) || !aligned(y_sorted, 16) || !aligned(workspace, 16) ||
         !aligned(offsets, 4) || !aligned(sorted_slot, 4) || !aligned(s_gate, 4) || !aligned(s_up, 4) ||
@@ -302,6 +305,9 @@ moe_status grouped_swiglu(bool with_x, const uint16_t* x, const uint8_t* xq_in, 
         DownArgs a{};
         a.hq = hq; a.hs = hs; a.rows = rows; a.d = d; a.d_ff = d_ff; a.wd = w_down; a.sd = s_down;
         a.tiles = tiles; a.num_tiles = ntiles; a.max_tiles = cap; a.y = y_sorted;
+        if (top1) {
+            a.scatter = sorted_slot; a.scatter_w = top1_w; a.out_rows = N;
+        }
         ProfScope ps(MOE_KERNEL_DOWN, s);
         MOE_HIP(launch_down(a, shape, s));
     }
@@ -336,6 +342,15 @@ moe_status moe_grouped_swiglu(const uint16_t* x, int64_t N, int32_t K, int32_t E
                               size_t workspace_bytes, uint32_t flags, void* stream) {
     return grouped_swiglu(true, x, nullptr, nullptr, N, K, E, d, d_ff, offsets, sorted_slot, w_gate, s_gate, w_up,
                           s_up, w_down, s_down, y_sorted, workspace, workspace_bytes, flags, stream);
+}
+
+moe_status moe_grouped_swiglu_top1(const uint16_t* x, int64_t N, int32_t E, int32_t d, int32_t d_ff,
+                                   const int32_t* offsets, const int32_t* sorted_slot, const float* topk_w,
+                                   const uint8_t* w_gate, const float* s_gate, const uint8_t* w_up,
+                                   const float* s_up, const uint8_t* w_down, const float* s_down, uint16_t* out,
+                                   void* workspace, size_t workspace_bytes, uint32_t flags, void* stream) {
+    return grouped_swiglu(true, x, nullptr, nullptr, N, 1, E, d, d_ff, offsets, sorted_slot, w_gate, s_gate, w_up,
+                          s_up, w_down, s_down, out, workspace, workspace_bytes, flags, stream, topk_w, true);
 }
 
 moe_status moe_grouped_swiglu_q(const uint8_t* xq, const float* xs, int64_t N, int32_t K, int32_t E, int32_t d,

@@ -43,7 +43,8 @@ struct GemmParams {
     const uint8_t* w1; const float* s1;   // up (gate|up only)
     const Tile* tiles; const int32_t* num_tiles;
     uint8_t* hq; float* hs;    // gate|up outputs [rows][d_ff], [rows][d_ff/128]
-    uint16_t* y;               // down output [rows][d] bf16
+    uint16_t* y;               // down output [rows][d] bf16 (or [out_rows][d] with scatter)
+    const int32_t* scatter; const float* scatter_w; int64_t out_rows;   // top-1 combine
 };
 
 __device__ __forceinline__ v8i load_frag_global(const uint8_t* p) {
@@ -276,10 +277,25 @@ __global__ __launch_bounds__(WM* WN * 64) void k_grouped_gemm(const GemmParams P
                 const int row = wm * MT * 16 + mt * 16 + 4 * (lane >> 4) + i;
                 if (row < nrows) {
                     const int64_t p = p0 + row;
+                    int64_t dst = p;
+                    float wgt = 1.0f;
+                    if (P.scatter) {   // top-1 combine: bf16(0 + w * bf16(y)), the combine's arithmetic
+                        dst = P.scatter[p];
+                        if (dst < 0 || dst >= P.out_rows) continue;
+                        wgt = P.scatter_w[dst];
+                    }
 #pragma unroll
                     for (int nt = 0; nt < NT; ++nt) {
                         const int col = wcol0 + nt * 16 + (lane & 15);
-                        if (col < P.Ndim) P.y[p * P.Ndim + col] = (uint16_t)f32_to_bf16(acc[0][mt][nt][i]);
+                        if (col < P.Ndim) {
+                            uint32_t v = f32_to_bf16(acc[0][mt][nt][i]);
+                            if (P.scatter) {
+                                float c = 0.0f;
+                                c += wgt * bf16_to_f32(v);
+                                v = f32_to_bf16(c);
+                            }
+                            P.y[dst * P.Ndim + col] = (uint16_t)v;
+                        }
                     }
                 }
             }
@@ -330,7 +346,7 @@ hipError_t launch_down(const DownArgs& a, TileShape shape, hipStream_t stream) {
     P.Kdim = a.d_ff; P.Ndim = a.d;
     P.w0 = a.wd; P.s0 = a.sd; P.w1 = nullptr; P.s1 = nullptr;
     P.tiles = a.tiles; P.num_tiles = a.num_tiles;
-    P.y = a.y;
+    P.y = a.y; P.scatter = a.scatter; P.scatter_w = a.scatter_w; P.out_rows = a.out_rows;
     switch (shape) {
         // 128 output columns per workgroup (two 16-column subtiles per wave): 96 registers,
         // so 5 waves per SIMD instead of 3 with four subtiles, and 3% faster at decode

@@ -89,6 +89,7 @@ struct Cfg {
     static_assert(A_Q * ROLE_W * 64 == BM * 8 && B_Q * ROLE_W * 64 == BR * 8, "copy split");
     static_assert(S_L <= 64 && BM % ROLE_W == 0, "scale copies");
     static_assert(LDS <= 160 * 1024, "LDS budget");
+    static_assert(2 * BM <= 2 * MAX_KB && BM <= THREADS, "the top-1 epilogue's row table");
     static_assert(NA >= 2 && NA <= 4 && NBS >= 2 && NBS <= 4, "ring depths");
     static_assert((NA - 2) * (A_Q + 1) <= 63 && (NBS - 2) * B_Q <= 63, "pending copies fit the wait counter");
 };
@@ -105,6 +106,7 @@ struct LdsGemmParams {
     const Tile* tiles; const int32_t* num_tiles;
     uint8_t* hq; float* hs;
     uint16_t* y;
+    const int32_t* scatter; const float* scatter_w; int64_t out_rows;   // top-1 combine (down)
 };
 
 // Byte offset of 16-B chunk c of row r in a swizzled [rows][128 B] LDS tile. A fragment read
@@ -570,7 +572,24 @@ __global__ __launch_bounds__(512) void k_gemm_lds(const LdsGemmParams P) {
             }
         }
     } else {
-        // ---- bf16 Y tile [BM][256] through LDS, coalesced 16-B stores of valid rows/columns
+        // ---- bf16 Y tile [BM][256] through LDS, coalesced 16-B stores of valid rows/columns.
+        // With the top-1 combine, each tile row's destination row and weight are read once
+        // (their loads overlap the staging) into the weight-scale table, unused from here on.
+        int32_t* const sDst = reinterpret_cast<int32_t*>(sSw);
+        float* const sWt = sSw + BM;
+        int32_t my_dst = -1;
+        float my_w = 0.0f;
+        if (P.scatter) {
+            for (int r = tid; r < BM; r += C::THREADS) {   // BM <= THREADS: one row per thread
+                if (r < nrows) {
+                    const int64_t d = P.scatter[p0 + r];
+                    if (d >= 0 && d < P.out_rows) {
+                        my_dst = (int32_t)d;
+                        my_w = P.scatter_w[d];
+                    }
+                }
+            }
+        }
         uint16_t* out = reinterpret_cast<uint16_t*>(smem);
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
@@ -583,13 +602,40 @@ __global__ __launch_bounds__(512) void k_gemm_lds(const LdsGemmParams P) {
                 *reinterpret_cast<uint2*>(out + row * kOutPitch + wn * 64 + j * 16 + 4 * kg) = v;
             }
         }
+        if (P.scatter && tid < BM) {
+            sDst[tid] = my_dst;
+            sWt[tid] = my_w;
+        }
         __syncthreads();
         const int ncols = P.Ndim - n0 < 256 ? P.Ndim - n0 : 256;
-        for (int c = tid; c < BM * 32; c += C::THREADS) {
-            const int row = c >> 5, cc = (c & 31) * 8;
-            if (row < nrows && cc < ncols)
-                *reinterpret_cast<uint4*>(P.y + (p0 + row) * P.Ndim + n0 + cc) =
-                    *reinterpret_cast<const uint4*>(out + row * kOutPitch + cc);
+        if (P.scatter) {
+            // top-1 combine: row p of the tile goes to row scatter[p] of y as
+            // bf16(0 + w * bf16(y)), the combine's arithmetic for one choice
+            for (int c = tid; c < BM * 32; c += C::THREADS) {
+                const int row = c >> 5, cc = (c & 31) * 8;
+                if (row >= nrows || cc >= ncols) continue;
+                const int64_t dst = sDst[row];
+                if (dst < 0) continue;
+                const float wgt = sWt[row];
+                const uint4 v = *reinterpret_cast<const uint4*>(out + row * kOutPitch + cc);
+                const uint32_t in[4] = {v.x, v.y, v.z, v.w};
+                uint32_t o[4];
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    float lo = 0.0f, hi = 0.0f;
+                    lo += wgt * bf16_to_f32(in[k] & 0xffffu);
+                    hi += wgt * bf16_to_f32(in[k] >> 16);
+                    o[k] = f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+                }
+                *reinterpret_cast<uint4*>(P.y + dst * P.Ndim + n0 + cc) = make_uint4(o[0], o[1], o[2], o[3]);
+            }
+        } else {
+            for (int c = tid; c < BM * 32; c += C::THREADS) {
+                const int row = c >> 5, cc = (c & 31) * 8;
+                if (row < nrows && cc < ncols)
+                    *reinterpret_cast<uint4*>(P.y + (p0 + row) * P.Ndim + n0 + cc) =
+                        *reinterpret_cast<const uint4*>(out + row * kOutPitch + cc);
+            }
         }
     }
 }
@@ -642,7 +688,7 @@ hipError_t launch_down_lds(const DownArgs& a, int rows, hipStream_t stream) {
     P.Kdim = a.d_ff; P.Ndim = a.d;
     P.w0 = a.wd; P.s0 = a.sd;
     P.tiles = a.tiles; P.num_tiles = a.num_tiles;
-    P.y = a.y;
+    P.y = a.y; P.scatter = a.scatter; P.scatter_w = a.scatter_w; P.out_rows = a.out_rows;
     switch (rows) {
         case 128: return launch_lds<1, 4>(P, a.max_tiles, stream);
         case 192: return launch_lds<1, 6>(P, a.max_tiles, stream);

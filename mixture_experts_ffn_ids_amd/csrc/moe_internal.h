@@ -120,7 +120,10 @@ struct DownArgs {
     int d, d_ff;
     const uint8_t* wd; const float* sd;
     const Tile* tiles; const int32_t* num_tiles; int64_t max_tiles;
-    uint16_t* y;            // [rows][d] bf16
+    uint16_t* y;            // [rows][d] bf16 in sorted order, or [out_rows][d] with scatter
+    // top-1 combine in the epilogue (NULL: none): sorted row p goes to row scatter[p] of y,
+    // times scatter_w[scatter[p]]; rows whose target lies outside [0, out_rows) are dropped
+    const int32_t* scatter; const float* scatter_w; int64_t out_rows;
 };
 
 hipError_t launch_gate_up(const GateUpArgs& a, TileShape shape, hipStream_t stream);

@@ -41,9 +41,9 @@
 // explicitly (s_waitcnt vmcnt) before the barrier that publishes a block.
 //
 // Scheduling: workgroups are dispatched round-robin over the 8 XCDs. The workgroup id is
-// remapped so that each XCD gets a contiguous range of (expert, n-block, row tile) items:
-// the row tiles that share a weight block, and the n-blocks that share a tile's rows, run
-// on the same XCD at about the same time and share its L2.
+// remapped so that each XCD gets a contiguous range of items ordered (expert, group of up to
+// 8 row tiles, n-block, row tile): the row tiles that share a weight block, and the n-blocks
+// that share a tile's rows, run on the same XCD at about the same time and share its L2.
 //
 // Epilogue: down results are staged through the (then idle) stage buffers and written with
 // coalesced 16-byte stores; gate|up codes go from registers straight to global memory.
@@ -59,6 +59,14 @@ namespace {
 constexpr int kXcds = 8;
 constexpr int kMaxDevices = 64;     // devices per process the launcher keeps state for
 constexpr int kOutPitch = 256 + 8;  // bf16 elements per row of the staged down-GEMM output
+// Row tiles of one expert that sweep its n-blocks together. An XCD runs about 32 consecutive
+// items at once (one workgroup per CU); 8 row tiles x 4 n-blocks is the window that fetches the
+// fewest activation and weight bytes per K block (8 x 16 KB + 4 x 32 KB at 128 rows, against
+// 30 x 16 KB + 32 KB when 30 row tiles of one n-block run together). Measured on the dense MLP
+// (43 row tiles of 192 rows): 3.7% faster step than sweeping all row tiles per n-block, 3% with
+// groups of 4; level on workloads whose experts have at most 8 row tiles, where the order is
+// unchanged.
+constexpr int kRowGroup = 8;
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
@@ -104,6 +112,7 @@ struct LdsGemmParams {
     const uint8_t* w0; const float* s0;
     const uint8_t* w1; const float* s1;
     const Tile* tiles; const int32_t* num_tiles;
+    int row_group;             // row tiles of one expert that sweep the n-blocks together
     uint8_t* hq; float* hs;
     uint16_t* y;
     const int32_t* scatter; const float* scatter_w; int64_t out_rows;   // top-1 combine (down)
@@ -189,16 +198,23 @@ __global__ __launch_bounds__(512) void k_gemm_lds(const LdsGemmParams P) {
     const int wm = wave >> 2, wn = wave & 3;
     const int n_blocks = MODE == 0 ? P.Ndim / 128 : (P.Ndim + 255) / 256;
 
-    // ---- XCD-aware work item (expert, n-block, row tile)
+    // ---- XCD-aware work item (expert, row-tile group, n-block, row tile)
     const int32_t ntile = *P.num_tiles;
     const int64_t work = (int64_t)ntile * n_blocks;
     const int64_t per_xcd = (work + kXcds - 1) / kXcds;
     const int64_t item = (int64_t)(blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
     if (blockIdx.x / kXcds >= per_xcd || item >= work) return;
     const Tile head = P.tiles[item / n_blocks];   // a tile of the item's expert
+    // within the expert: groups of up to P.row_group row tiles, each group's (n-block, row
+    // tile) items in that order, row tile fastest
     const int64_t local = item - (int64_t)n_blocks * head.first;
-    const int nb = (int)(local / head.count);
-    const int t = head.first + (int)(local % head.count);
+    const int64_t gspan = (int64_t)P.row_group * n_blocks;
+    const int g = (int)(local / gspan);
+    const int r = (int)(local - g * gspan);
+    const int grem = head.count - g * P.row_group;
+    const int gsize = grem < P.row_group ? grem : P.row_group;
+    const int nb = r / gsize;
+    const int t = head.first + g * P.row_group + r % gsize;
     if (t >= ntile) return;
     const Tile tile = P.tiles[t];
     const int e = tile.expert;
@@ -641,8 +657,9 @@ __global__ __launch_bounds__(512) void k_gemm_lds(const LdsGemmParams P) {
 }
 
 template <int MODE, int MT>
-hipError_t launch_lds(const LdsGemmParams& P, int64_t max_tiles, hipStream_t stream) {
+hipError_t launch_lds(LdsGemmParams P, int64_t max_tiles, hipStream_t stream) {
     using C = Cfg<MODE, MT>;
+    P.row_group = kRowGroup;
     const int64_t n_blocks = MODE == 0 ? P.Ndim / 128 : (P.Ndim + 255) / 256;
     int64_t grid = max_tiles * n_blocks;
     grid = (grid + kXcds - 1) / kXcds * kXcds;

@@ -286,10 +286,11 @@ moe_status grouped_swiglu(bool with_x, const uint16_t* x, const uint8_t* xq_in, 
     const int64_t cap = max_tiles(rows, E, BM);
 
     if (with_x) {
+        // the tile list is built by the last workgroup of the quantisation launch
+        const TileJob job{offsets, E, rows, BM, cap, tiles, ntiles};
         ProfScope ps(MOE_KERNEL_QUANT, s);
-        MOE_HIP(launch_quantize_rows(x, N, d, ws + L.xq, (float*)(ws + L.xs), s));
-    }
-    {
+        MOE_HIP(launch_quantize_rows(x, N, d, ws + L.xq, (float*)(ws + L.xs), s, &job));
+    } else {
         ProfScope ps(MOE_KERNEL_DISPATCH, s);
         MOE_HIP(launch_build_tiles(offsets, E, rows, BM, cap, tiles, ntiles, s));
     }

@@ -3,7 +3,9 @@
 // the scatter-of-ones column sum, the argsort of the flat ids and the running
 // start/end index of each expert's slice).
 //
-// Integer-only and deterministic. Four launches:
+// Integer-only and deterministic. Batches of at most kSmallDispatch slots take one
+// launch (k_dispatch_small: one workgroup counts, scans and places every slot, walking the
+// slots in order); larger ones take four:
 //   1. k_hist:    slots are cut into chunks of 256; each workgroup counts its
 //                 chunk per expert in LDS (integer LDS atomics -- the counts do not
 //                 depend on their order) and writes chunk_counts[E][chunk].
@@ -41,30 +43,6 @@ __global__ __launch_bounds__(kDispatchChunk) void k_hist(const int32_t* __restri
     }
     __syncthreads();
     for (int e = threadIdx.x; e < E; e += blockDim.x) chunk_counts[(int64_t)e * nchunks + blockIdx.x] = cnt[e];
-}
-
-// Block-wide exclusive scan of one value per thread (up to 1024 threads = 16 waves).
-template <typename T>
-__device__ T block_exclusive_scan(T v, T* total) {
-    __shared__ T wsum[16];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    T incl = v;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        T t = __shfl_up(incl, off, 64);
-        if (lane >= off) incl += t;
-    }
-    if (lane == 63) wsum[wave] = incl;
-    __syncthreads();
-    T base = 0, all = 0;
-    const int nw = blockDim.x >> 6;
-    for (int w = 0; w < nw; ++w) {
-        if (w < wave) base += wsum[w];
-        all += wsum[w];
-    }
-    __syncthreads();
-    *total = all;
-    return base + incl - v;
 }
 
 // Per expert (one wave each, four per workgroup): exclusive prefix of its chunk counts, in
@@ -135,6 +113,85 @@ __global__ __launch_bounds__(kDispatchChunk) void k_permute(const int32_t* __res
     slot_pos[s] = p;
 }
 
+// One workgroup of 1024 threads (16 waves) does the whole dispatch of a small batch.
+//   1. counts in LDS (integer LDS atomics, one per expert and wave: the totals do not depend
+//      on their order);
+//   2. counts[e], and offsets[E+1] by a block scan; base[e] = offsets[e] in LDS;
+//   3. the slots in rounds of 1024, in slot order. Each lane finds the lanes of its wave with
+//      the same expert by one ballot per bit of the expert id; its rank among them gives its
+//      place after the earlier lanes. The 16 waves of a round then take their places in wave
+//      order, each advancing base[e] by its count of e, so positions follow slot order within
+//      each expert (the stable sort).
+// Out-of-range ids are not counted and get slot_pos = -1, as in the four-launch path.
+__global__ __launch_bounds__(1024) void k_dispatch_small(const int32_t* __restrict__ ids, int NK, int E,
+                                                         int nbits, int32_t* __restrict__ counts,
+                                                         int32_t* __restrict__ offsets,
+                                                         int32_t* __restrict__ sorted_slot,
+                                                         int32_t* __restrict__ slot_pos) {
+    extern __shared__ int32_t lds[];
+    int32_t* const cnt = lds;       // [E]
+    int32_t* const base = lds + E;  // [E]
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    for (int e = tid; e < E; e += 1024) cnt[e] = 0;
+    __syncthreads();
+    // lanes of this wave whose slot holds the same in-range expert as this lane's (valid lanes)
+    auto same_expert = [&](int32_t e, bool valid) -> uint64_t {
+        uint64_t match = __ballot(valid);
+        for (int b = 0; b < nbits; ++b) {
+            const bool bit = valid && ((e >> b) & 1);
+            const uint64_t m = __ballot(bit);
+            match &= bit ? m : ~m;
+        }
+        return match;
+    };
+    // one LDS atomic per expert and wave (the highest lane of each group adds the group's size),
+    // so that many slots of one expert do not serialise on one address
+    for (int r0 = 0; r0 < NK; r0 += 1024) {
+        const int s = r0 + tid;
+        const int32_t e = s < NK ? ids[s] : -1;
+        const bool valid = e >= 0 && e < E;
+        const uint64_t match = same_expert(e, valid);
+        if (valid && (match >> lane) == 1ull) atomicAdd(&cnt[e], __popcll(match));
+    }
+    __syncthreads();
+    // exclusive scan: thread tid owns experts [tid per, (tid+1) per)
+    const int per = (E + 1023) / 1024;
+    const int e0 = tid * per;
+    int32_t local = 0;
+    for (int e = e0; e < e0 + per && e < E; ++e) local += cnt[e];
+    int32_t total;
+    int32_t run = block_exclusive_scan<int32_t>(local, &total);
+    for (int e = e0; e < e0 + per && e < E; ++e) {
+        counts[e] = cnt[e];
+        offsets[e] = run;
+        base[e] = run;
+        run += cnt[e];
+    }
+    if (tid == 0) offsets[E] = total;
+    __syncthreads();
+    const uint64_t below = (1ull << lane) - 1ull;
+    for (int r0 = 0; r0 < NK; r0 += 1024) {
+        const int s = r0 + tid;
+        const int32_t e = s < NK ? ids[s] : -1;
+        const bool valid = e >= 0 && e < E;
+        const uint64_t match = same_expert(e, valid);
+        const int rank = __popcll(match & below);
+        const int n_same = __popcll(match);
+        const bool last = valid && (match >> lane) == 1ull;   // highest lane of its group
+        for (int w = 0; w < 16; ++w) {
+            if (wave == w && valid) {
+                const int32_t b0 = base[e];
+                const int32_t p = b0 + rank;
+                if (last) base[e] = b0 + n_same;
+                sorted_slot[p] = s;
+                slot_pos[s] = p;
+            }
+            __syncthreads();
+        }
+        if (s < NK && !valid) slot_pos[s] = -1;
+    }
+}
+
 __global__ void k_fill_i32(int32_t* p, int64_t n, int32_t v) {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i < n) p[i] = v;
@@ -145,6 +202,13 @@ hipError_t launch_dispatch(const int32_t* ids, int64_t N, int K, int E, int32_t*
                            int32_t* chunk_counts, int32_t* err_flag, bool checked,
                            hipStream_t stream) {
     const int64_t NK = N * K;
+    if (!checked && NK <= kSmallDispatch && E <= kSmallDispatchExperts) {
+        int nbits = 0;
+        while ((1 << nbits) < E) ++nbits;   // ids 0..E-1 fit nbits bits
+        hipLaunchKernelGGL(k_dispatch_small, dim3(1), dim3(1024), 2 * (size_t)E * sizeof(int32_t), stream, ids,
+                           (int)NK, E, nbits, counts, offsets, sorted_slot, slot_pos);
+        return hipGetLastError();
+    }
     const int nchunks = (int)((NK + kDispatchChunk - 1) / kDispatchChunk);
     if (checked) hipLaunchKernelGGL(k_fill_i32, dim3(1), dim3(64), 0, stream, err_flag, (int64_t)1, 0);
     if (nchunks > 0) {
@@ -168,49 +232,10 @@ int64_t max_tiles(int64_t rows, int E, int BM) {
     return rows / BM + nonempty + 1;
 }
 
-// num_tiles[0]: tiles written; num_tiles[1]: 1 when every expert with rows got one tile
 __global__ __launch_bounds__(1024) void k_tiles(const int32_t* __restrict__ offsets, int E, int64_t rows,
                                                 int BM, int64_t cap, Tile* __restrict__ tiles,
                                                 int32_t* __restrict__ num_tiles) {
-    // each thread owns a contiguous range of experts; offsets are clamped to [0, rows]
-    // so that any offsets array yields in-bounds tiles
-    const int per = (E + blockDim.x - 1) / blockDim.x;
-    const int e0 = threadIdx.x * per;
-    int64_t local = 0, local_busy = 0;
-    for (int e = e0; e < e0 + per && e < E; ++e) {
-        int64_t b = offsets[e], en = offsets[e + 1];
-        b = b < 0 ? 0 : (b > rows ? rows : b);
-        en = en < b ? b : (en > rows ? rows : en);
-        local += (en - b + BM - 1) / BM;
-        local_busy += en > b ? 1 : 0;
-    }
-    int64_t total, busy;
-    block_exclusive_scan<int64_t>(local_busy, &busy);
-    int64_t t = block_exclusive_scan<int64_t>(local, &total);
-    for (int e = e0; e < e0 + per && e < E; ++e) {
-        int64_t b = offsets[e], en = offsets[e + 1];
-        b = b < 0 ? 0 : (b > rows ? rows : b);
-        en = en < b ? b : (en > rows ? rows : en);
-        const int64_t first = t;
-        const int64_t count = (en - b + BM - 1) / BM;
-        // stops at the cap, so arbitrary offsets cannot make this loop long
-        for (int64_t r = b; r < en && t < cap; r += BM, ++t) {
-            Tile tl;
-            tl.expert = e;
-            tl.row_begin = (int32_t)r;
-            tl.row_end = (int32_t)(r + BM < en ? r + BM : en);
-            tl.first = (int32_t)first;
-            tl.count = (int32_t)count;
-            tl.pad[0] = tl.pad[1] = tl.pad[2] = 0;
-            tiles[t] = tl;
-        }
-    }
-    if (threadIdx.x == 0) {
-        num_tiles[0] = (int32_t)(total < cap ? total : cap);
-        // every expert with rows fits one tile: each weight block is then read by one
-        // workgroup only
-        num_tiles[1] = total == busy && total <= cap ? 1 : 0;
-    }
+    build_tiles_block(offsets, E, rows, BM, cap, tiles, num_tiles);
 }
 
 hipError_t launch_build_tiles(const int32_t* offsets, int E, int64_t rows, int BM, int64_t cap, Tile* tiles,

@@ -68,12 +68,13 @@ __device__ __forceinline__ v4f mfma_16x16x128_fp8(const v8i& a, const v8i& b) {
 }
 
 // ---------------------------------------------------------------- launchers
-hipError_t launch_quantize_rows(const uint16_t* x, int64_t rows, int cols, uint8_t* q, float* s,
-                                hipStream_t stream);
+
 hipError_t launch_rmsnorm_quantize(const uint16_t* x, const uint16_t* gain, float eps, int64_t rows, int cols,
                                    uint16_t* y, uint8_t* q, float* s, hipStream_t stream);
 
 constexpr int kDispatchChunk = 256;
+constexpr int kSmallDispatch = 8192;         // slots up to which one workgroup does the whole dispatch
+constexpr int kSmallDispatchExperts = 4096;  // and experts (its two LDS tables stay within 32 KB)
 hipError_t launch_dispatch(const int32_t* ids, int64_t N, int K, int E, int32_t* counts,
                            int32_t* offsets, int32_t* sorted_slot, int32_t* slot_pos,
                            int32_t* chunk_counts, int32_t* err_flag, bool checked,
@@ -91,6 +92,85 @@ struct Tile {
 };
 
 int64_t max_tiles(int64_t rows, int E, int BM);
+
+// Block-wide exclusive scan of one value per thread (up to 1024 threads = 16 waves).
+template <typename T>
+__device__ T block_exclusive_scan(T v, T* total) {
+    __shared__ T wsum[16];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    T incl = v;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        T t = __shfl_up(incl, off, 64);
+        if (lane >= off) incl += t;
+    }
+    if (lane == 63) wsum[wave] = incl;
+    __syncthreads();
+    T base = 0, all = 0;
+    const int nw = blockDim.x >> 6;
+    for (int w = 0; w < nw; ++w) {
+        if (w < wave) base += wsum[w];
+        all += wsum[w];
+    }
+    __syncthreads();
+    *total = all;
+    return base + incl - v;
+}
+
+// num_tiles[0]: tiles written; num_tiles[1]: 1 when every expert with rows got one tile
+// Run by one whole workgroup (any size up to 1024 threads, a multiple of 64).
+__device__ inline void build_tiles_block(const int32_t* __restrict__ offsets, int E, int64_t rows, int BM,
+                                         int64_t cap, Tile* __restrict__ tiles, int32_t* __restrict__ num_tiles) {
+    // each thread owns a contiguous range of experts; offsets are clamped to [0, rows]
+    // so that any offsets array yields in-bounds tiles
+    const int per = (E + blockDim.x - 1) / blockDim.x;
+    const int e0 = threadIdx.x * per;
+    int64_t local = 0, local_busy = 0;
+    for (int e = e0; e < e0 + per && e < E; ++e) {
+        int64_t b = offsets[e], en = offsets[e + 1];
+        b = b < 0 ? 0 : (b > rows ? rows : b);
+        en = en < b ? b : (en > rows ? rows : en);
+        local += (en - b + BM - 1) / BM;
+        local_busy += en > b ? 1 : 0;
+    }
+    int64_t total, busy;
+    block_exclusive_scan<int64_t>(local_busy, &busy);
+    int64_t t = block_exclusive_scan<int64_t>(local, &total);
+    for (int e = e0; e < e0 + per && e < E; ++e) {
+        int64_t b = offsets[e], en = offsets[e + 1];
+        b = b < 0 ? 0 : (b > rows ? rows : b);
+        en = en < b ? b : (en > rows ? rows : en);
+        const int64_t first = t;
+        const int64_t count = (en - b + BM - 1) / BM;
+        // stops at the cap, so arbitrary offsets cannot make this loop long
+        for (int64_t r = b; r < en && t < cap; r += BM, ++t) {
+            Tile tl;
+            tl.expert = e;
+            tl.row_begin = (int32_t)r;
+            tl.row_end = (int32_t)(r + BM < en ? r + BM : en);
+            tl.first = (int32_t)first;
+            tl.count = (int32_t)count;
+            tl.pad[0] = tl.pad[1] = tl.pad[2] = 0;
+            tiles[t] = tl;
+        }
+    }
+    if (threadIdx.x == 0) {
+        num_tiles[0] = (int32_t)(total < cap ? total : cap);
+        // every expert with rows fits one tile: each weight block is then read by one
+        // workgroup only
+        num_tiles[1] = total == busy && total <= cap ? 1 : 0;
+    }
+}
+
+
+// A tile list to build (build_tiles_block's arguments); tiles == NULL: none.
+struct TileJob {
+    const int32_t* offsets; int E; int64_t rows; int BM; int64_t cap; Tile* tiles; int32_t* num_tiles;
+};
+
+// Dynamic e4m3 quantisation of rows; with tile_job, the same launch also builds that tile list.
+hipError_t launch_quantize_rows(const uint16_t* x, int64_t rows, int cols, uint8_t* q, float* s,
+                                hipStream_t stream, const TileJob* tile_job = nullptr);
 
 // num_tiles[2]: the number of tiles, and 1 if every expert with rows got exactly one tile
 hipError_t launch_build_tiles(const int32_t* offsets, int E, int64_t rows, int BM, int64_t max_tiles,

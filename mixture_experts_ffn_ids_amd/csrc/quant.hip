@@ -28,12 +28,18 @@ __device__ __forceinline__ void quant_group(const uint4 raw, uint2& codes, float
 }
 
 // Each 16-lane group quantises two consecutive 128-value groups per step (both loads in
-// flight before either is reduced).
+// flight before either is reduced). With a tile job, the last workgroup builds the GEMM tile
+// list instead (it does not depend on the quantised rows), which saves a launch.
 __global__ __launch_bounds__(256) void k_quantize_rows(const uint16_t* __restrict__ x, int64_t groups,
                                                        int cols, uint8_t* __restrict__ q,
-                                                       float* __restrict__ s) {
+                                                       float* __restrict__ s, const TileJob job) {
+    const int qblocks = gridDim.x - (job.tiles ? 1 : 0);
+    if ((int)blockIdx.x == qblocks) {   // only with a tile job
+        build_tiles_block(job.offsets, job.E, job.rows, job.BM, job.cap, job.tiles, job.num_tiles);
+        return;
+    }
     const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    const int64_t stride = (int64_t)qblocks * blockDim.x;
     const int sub = threadIdx.x & 15;
     const int gpr = cols / kGroup;  // groups per row
     const int64_t pairs = (groups + 1) / 2;
@@ -63,6 +69,10 @@ __global__ __launch_bounds__(256) void k_quantize_rows(const uint16_t* __restric
             }
         }
     }
+}
+
+__global__ __launch_bounds__(256) void k_tiles_only(const TileJob job) {
+    build_tiles_block(job.offsets, job.E, job.rows, job.BM, job.cap, job.tiles, job.num_tiles);
 }
 
 // RMSNorm of a bfloat16 row with a bfloat16 gain, fused with the e4m3 quantisation of the
@@ -169,13 +179,19 @@ hipError_t launch_rmsnorm_quantize(const uint16_t* x, const uint16_t* gain, floa
 }
 
 hipError_t launch_quantize_rows(const uint16_t* x, int64_t rows, int cols, uint8_t* q, float* s,
-                                hipStream_t stream) {
+                                hipStream_t stream, const TileJob* tile_job) {
     const int64_t groups = rows * (cols / kGroup);
-    if (groups == 0) return hipSuccess;
+    const TileJob job = tile_job ? *tile_job : TileJob{};
+    if (groups == 0) {
+        if (job.tiles)
+            hipLaunchKernelGGL(k_tiles_only, dim3(1), dim3(256), 0, stream, job);
+        return hipGetLastError();
+    }
     const int64_t threads = (groups + 1) / 2 * 16;
     int64_t blocks = (threads + 255) / 256;
     if (blocks > 65536) blocks = 65536;
-    hipLaunchKernelGGL(k_quantize_rows, dim3((unsigned)blocks), dim3(256), 0, stream, x, groups, cols, q, s);
+    if (job.tiles) ++blocks;
+    hipLaunchKernelGGL(k_quantize_rows, dim3((unsigned)blocks), dim3(256), 0, stream, x, groups, cols, q, s, job);
     return hipGetLastError();
 }
 

@@ -94,3 +94,35 @@ def test_dispatch_deterministic():
     for x, y in ((a.counts, b.counts), (a.offsets, b.offsets), (a.sorted_slot, b.sorted_slot),
                  (a.slot_pos, b.slot_pos)):
         assert torch.equal(x, y)
+
+
+@pytest.mark.parametrize("n, k, E", [(1024, 8, 384), (1025, 8, 384), (2, 1, 4096), (2, 1, 4097),
+                                     (1000, 8, 4096), (8191, 1, 3)],
+                         ids=["8192-slots", "8200-slots", "E4096", "E4097", "8000-slots-E4096", "8191-slots-E3"])
+def test_dispatch_at_the_one_workgroup_limits(n, k, E):
+    """Batches of at most 8192 slots and 4096 experts take the one-workgroup dispatch, larger
+    ones the four-launch path; both must give the oracle's result on either side of the limits."""
+    rng = np.random.default_rng(n * 31 + E)
+    ids = np.argsort(rng.random((n, E)), 1)[:, :k].astype(np.int32) if E <= 512 else \
+        np.stack([rng.choice(E, size=k, replace=False) for _ in range(n)]).astype(np.int32)
+    _assert_same(ids, E)
+
+
+@pytest.mark.parametrize("n", [7, 1500], ids=["one-wave", "two-rounds"])
+def test_dispatch_unchecked_bad_ids_small_batch(n):
+    """The one-workgroup dispatch leaves out-of-range slots out like the four-launch path:
+    counts of the valid ids only, valid slots in stable order, slot_pos = -1 for the rest
+    (compared with numpy's bincount and stable argsort)."""
+    E = 6
+    rng = np.random.default_rng(n)
+    ids = rng.integers(-2, E + 2, size=(n, 2)).astype(np.int32)
+    say(f"dispatch unchecked bad ids N={n}")
+    d = _run(ids, E)
+    flat = ids.ravel()
+    valid = (flat >= 0) & (flat < E)
+    order = np.nonzero(valid)[0][np.argsort(flat[valid], kind="stable")]
+    pos = np.full(flat.size, -1, np.int64)
+    pos[order] = np.arange(order.size)
+    assert np.array_equal(d.counts.cpu().numpy(), np.bincount(flat[valid], minlength=E))
+    assert np.array_equal(d.sorted_slot.cpu().numpy()[:order.size], order)
+    assert np.array_equal(d.slot_pos.cpu().numpy(), pos)

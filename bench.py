@@ -43,8 +43,8 @@ FP8_PEAK_TFLOPS = 5000.0       # MI355X dense FP8 matrix peak (no sparsity)
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="k2_decode_256")
     ap.add_argument("--cpu-tokens", type=int, default=None,
                     help="rows of x in the oracle's CPU-baseline sample (default: whole batch up to "

@@ -225,7 +225,8 @@ def main():
     n_sh = 1 if cfg.shared else 0
     w_proj = d * d_ff                                   # bytes of one fp8 projection
     s_proj = (d // 128) * (d_ff // 128) * 4             # its block scales
-    # gate|up launches: one for the routed experts (+ one for the shared expert)
+    # gate|up launches: one for the routed experts (+ one for the shared expert, which runs on a
+    # second stream alongside the routed launches, so that its launch times include the overlap)
     gu_bytes_routed = touched * 2 * (w_proj + s_proj) + N * d + N * (d // 128) * 4 + N * K * d_ff + N * K * (d_ff // 128) * 4
     gu_bytes_shared = n_sh * (2 * (w_proj + s_proj) + N * d + N * (d // 128) * 4 + N * d_ff + N * (d_ff // 128) * 4)
     gu_launches_per_step = 1 + n_sh

@@ -83,7 +83,7 @@ def quantize_rows(x: torch.Tensor):
     return q, s
 
 
-def dispatch(topk_ids: torch.Tensor, E: int, checked: bool = False) -> Dispatch:
+def dispatch(topk_ids: torch.Tensor, E: int, checked: bool = False, _ws_tag: str = "dispatch") -> Dispatch:
     _want(topk_ids, torch.int32, "topk_ids", 2)
     N, K = topk_ids.shape
     dev = topk_ids.device
@@ -92,16 +92,29 @@ def dispatch(topk_ids: torch.Tensor, E: int, checked: bool = False) -> Dispatch:
     sorted_slot = torch.empty(N * K, dtype=torch.int32, device=dev)
     slot_pos = torch.empty(N * K, dtype=torch.int32, device=dev)
     nb = lib().moe_dispatch_workspace_size(N, K, E)
-    ws = _workspace(nb, dev, "dispatch")
+    ws = _workspace(nb, dev, _ws_tag)
     st = lib().moe_dispatch(_p(topk_ids), N, K, E, _p(counts), _p(offsets), _p(sorted_slot), _p(slot_pos),
                             _p(ws), ws.numel(), FLAG_CHECKED if checked else 0, _stream(dev))
     check(st, "moe_dispatch")
     return Dispatch(counts, offsets, sorted_slot, slot_pos, N, K, E)
 
 
-def identity_dispatch(N: int, device) -> Dispatch:
+def identity_dispatch(N: int, device, _ws_tag: str = "dispatch") -> Dispatch:
     """Dispatch of every token to a single expert (E = 1, K = 1): the shared expert's rows."""
-    return dispatch(torch.zeros((N, 1), dtype=torch.int32, device=device), 1)
+    return dispatch(torch.zeros((N, 1), dtype=torch.int32, device=device), 1, _ws_tag=_ws_tag)
+
+
+_SIDE: dict = {}
+
+
+def _side_stream(dev: torch.device) -> torch.cuda.Stream:
+    """A second stream per device (default priority) for the shared expert."""
+    key = str(dev)
+    s = _SIDE.get(key)
+    if s is None:
+        s = torch.cuda.Stream(device=dev)
+        _SIDE[key] = s
+    return s
 
 
 def _expert_dims(experts, d: int, N: int, disp: Dispatch):
@@ -131,7 +144,7 @@ def _y_out(out, rows: int, d: int, device):
 
 
 def grouped_swiglu(x: torch.Tensor, disp: Dispatch, experts, flags: int = 0,
-                   out: torch.Tensor | None = None) -> torch.Tensor:
+                   out: torch.Tensor | None = None, _ws_tag: str = "swiglu") -> torch.Tensor:
     """y_sorted [N*K, d] bf16: each sorted row through its expert's SwiGLU MLP (unweighted)."""
     _want(x, torch.bfloat16, "x", 2)
     N, d = x.shape
@@ -139,7 +152,7 @@ def grouped_swiglu(x: torch.Tensor, disp: Dispatch, experts, flags: int = 0,
     ex, K = experts, disp.K
     out = _y_out(out, N * K, d, x.device)
     nb = lib().moe_swiglu_workspace_size(N, K, E, d, d_ff)
-    ws = _workspace(nb, x.device, "swiglu")
+    ws = _workspace(nb, x.device, _ws_tag)
     st = lib().moe_grouped_swiglu(_p(x), N, K, E, d, d_ff, _p(disp.offsets), _p(disp.sorted_slot),
                                   _p(ex.w_gate), _p(ex.s_gate), _p(ex.w_up), _p(ex.s_up), _p(ex.w_down),
                                   _p(ex.s_down), _p(out), _p(ws), ws.numel(), int(flags), _stream(x.device))
@@ -148,7 +161,7 @@ def grouped_swiglu(x: torch.Tensor, disp: Dispatch, experts, flags: int = 0,
 
 
 def grouped_swiglu_q(xq: torch.Tensor, xs: torch.Tensor, disp: Dispatch, experts, flags: int = 0,
-                     out: torch.Tensor | None = None) -> torch.Tensor:
+                     out: torch.Tensor | None = None, _ws_tag: str = "swiglu") -> torch.Tensor:
     """grouped_swiglu on activations already quantised: xq [N, d] uint8 e4m3 codes and
     xs [N, d/128] float32 scales, as quantize_rows or rmsnorm_quantize write them."""
     _want(xq, torch.uint8, "xq", 2)
@@ -160,7 +173,7 @@ def grouped_swiglu_q(xq: torch.Tensor, xs: torch.Tensor, disp: Dispatch, experts
     ex, K = experts, disp.K
     out = _y_out(out, N * K, d, xq.device)
     nb = lib().moe_swiglu_q_workspace_size(N, K, E, d, d_ff)
-    ws = _workspace(nb, xq.device, "swiglu")
+    ws = _workspace(nb, xq.device, _ws_tag)
     st = lib().moe_grouped_swiglu_q(_p(xq), _p(xs), N, K, E, d, d_ff, _p(disp.offsets), _p(disp.sorted_slot),
                                     _p(ex.w_gate), _p(ex.s_gate), _p(ex.w_up), _p(ex.s_up), _p(ex.w_down),
                                     _p(ex.s_down), _p(out), _p(ws), ws.numel(), int(flags), _stream(xq.device))
@@ -249,11 +262,22 @@ def moe_layer(x: torch.Tensor, topk_ids: torch.Tensor, topk_w: torch.Tensor, exp
     if disp.K == 1 and shared_expert is None:
         # one choice per token: the combine is done by the down projection's epilogue
         return grouped_swiglu_top1(x, disp, topk_w, experts, flags)
-    y = grouped_swiglu(x, disp, experts, flags)
     shared = None
     if shared_expert is not None:
-        sdisp = identity_dispatch(x.shape[0], x.device)
-        shared = grouped_swiglu(x, sdisp, shared_expert)
+        # the shared expert is independent of the routed experts until the combine: it runs on
+        # a second stream (with workspaces of its own), so that its small launches fill the
+        # routed launches' idle CUs instead of queueing behind them
+        main = torch.cuda.current_stream(x.device)
+        side = _side_stream(x.device)
+        side.wait_stream(main)
+        x.record_stream(side)
+        with torch.cuda.stream(side):
+            sdisp = identity_dispatch(x.shape[0], x.device, _ws_tag="dispatch_shared")
+            shared = grouped_swiglu(x, sdisp, shared_expert, _ws_tag="swiglu_shared")
+        shared.record_stream(main)
+    y = grouped_swiglu(x, disp, experts, flags)
+    if shared is not None:
+        torch.cuda.current_stream(x.device).wait_stream(_side_stream(x.device))
     return combine(y, disp, topk_w, shared)
 
 
@@ -267,11 +291,21 @@ def moe_block_ffn(hidden: torch.Tensor, gain: torch.Tensor, eps: float, topk_ids
     E = experts.w_gate.shape[0]
     xq, xs, _ = rmsnorm_quantize(hidden, gain, eps)
     disp = dispatch(topk_ids, E)
-    y = grouped_swiglu_q(xq, xs, disp, experts, flags)
     shared = None
     if shared_expert is not None:
-        sdisp = identity_dispatch(hidden.shape[0], hidden.device)
-        shared = grouped_swiglu_q(xq, xs, sdisp, shared_expert)
+        # on a second stream, as in moe_layer
+        main = torch.cuda.current_stream(hidden.device)
+        side = _side_stream(hidden.device)
+        side.wait_stream(main)
+        xq.record_stream(side)
+        xs.record_stream(side)
+        with torch.cuda.stream(side):
+            sdisp = identity_dispatch(hidden.shape[0], hidden.device, _ws_tag="dispatch_shared")
+            shared = grouped_swiglu_q(xq, xs, sdisp, shared_expert, _ws_tag="swiglu_shared")
+        shared.record_stream(main)
+    y = grouped_swiglu_q(xq, xs, disp, experts, flags)
+    if shared is not None:
+        torch.cuda.current_stream(hidden.device).wait_stream(_side_stream(hidden.device))
     return combine(y, disp, topk_w, shared, out=out, residual=hidden)
 
 

@@ -17,11 +17,12 @@
 // scale) and added to the float32 accumulator -- the block-scale dequantisation
 // happens in the accumulator, never on the operands.
 //
-// Operands: the activation tile (BM x 128 bytes per K block) is staged through
-// LDS (double-buffered, rows padded to 144 bytes so 16 rows read at one column
-// fall in distinct banks) because every wave of the workgroup reads it; each
-// weight byte is needed by one wave only, so weights go straight from HBM into
-// the MFMA operand registers, one K block ahead of use.
+// Operands: each weight byte is needed by one wave only, and the tile's few token
+// rows (16) are read by every wave from L2, so both go straight from memory into
+// the MFMA operand registers, one K block ahead of use, in two register sets used
+// in turn: a wave never waits for the block it has just asked for, and no barrier
+// couples the waves inside the K loop. (Staging the token rows through LDS made
+// every K block end in a full wait for the next block's loads and a barrier.)
 //
 // Any 16x16x128 operand layout works as long as A and B use the same one: lane l
 // supplies row (l & 15) and the 32 K-values [32*(l>>4), 32*(l>>4)+32) of its
@@ -29,8 +30,6 @@
 #include "moe_internal.h"
 
 namespace moe {
-
-constexpr int kAPitch = 144;  // LDS bytes per activation row (128 + 16 pad)
 
 struct GemmParams {
     const uint8_t* a;          // activation codes, row stride Kdim
@@ -56,14 +55,6 @@ __device__ __forceinline__ v8i load_frag_global(const uint8_t* p) {
     return r;
 }
 
-__device__ __forceinline__ v8i load_frag_lds(const uint8_t* p) {
-    const uint4* q = reinterpret_cast<const uint4*>(p);
-    const uint4 lo = q[0], hi = q[1];
-    v8i r;
-    r[0] = lo.x; r[1] = lo.y; r[2] = lo.z; r[3] = lo.w;
-    r[4] = hi.x; r[5] = hi.y; r[6] = hi.z; r[7] = hi.w;
-    return r;
-}
 
 
 // MODE 0: gate|up with the silu*up requant epilogue; MODE 1: down with bf16 output.
@@ -73,17 +64,15 @@ __global__ __launch_bounds__(WM* WN * 64) void k_grouped_gemm(const GemmParams P
     constexpr int BM = WM * MT * 16;
     constexpr int BN = WN * NT * 16;
     constexpr int THREADS = WM * WN * 64;
-    constexpr int A_CHUNKS = BM * 8;  // 16-byte chunks per activation K block
-    constexpr int A_PER_THREAD = (A_CHUNKS + THREADS - 1) / THREADS;
     static_assert(128 % (NT * 16) == 0, "a wave's columns must sit in one 128-wide scale block");
     static_assert(MODE == 1 || BN == 128, "gate|up requantises whole 128-column groups");
 
-    __shared__ __attribute__((aligned(16))) uint8_t sA[2][BM * kAPitch];
-    __shared__ float sAs[2][BM];
     __shared__ int32_t sRow[BM];
     __shared__ float sRed[MODE == 0 ? WN : 1][BM];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    // the wave index is uniform within a wave: what derives from it stays in scalar registers
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / WN, wn = wave % WN;
     const int n_blocks = (P.Ndim + BN - 1) / BN;
     const int64_t t = blockIdx.x / n_blocks;
@@ -97,78 +86,72 @@ __global__ __launch_bounds__(WM* WN * 64) void k_grouped_gemm(const GemmParams P
     const int KB = P.Kdim / 128;
     const int NB128 = P.Ndim / 128;
 
+    // source row of every tile row; rows past the end of the tile repeat its first row (their
+    // results are never stored)
     for (int r = tid; r < BM; r += THREADS) {
-        int32_t src = -1;
-        if (r < nrows) {
-            const int64_t p = p0 + r;
-            if (MODE == 0) {
-                int64_t tok = P.gather[p] / P.K_top;
-                tok = tok < 0 ? 0 : (tok >= P.src_rows ? P.src_rows - 1 : tok);
-                src = (int32_t)tok;
-            } else {
-                src = (int32_t)p;
-            }
+        const int64_t p = p0 + (r < nrows ? r : 0);
+        int32_t src;
+        if (MODE == 0) {
+            int64_t tok = P.gather[p] / P.K_top;
+            tok = tok < 0 ? 0 : (tok >= P.src_rows ? P.src_rows - 1 : tok);
+            src = (int32_t)tok;
+        } else {
+            src = (int32_t)p;
         }
         sRow[r] = src;
     }
     __syncthreads();
 
-    // ---- activation tile staging
-    uint4 aReg[A_PER_THREAD];
-    float asReg[(BM + THREADS - 1) / THREADS];
-    auto loadA = [&](int kb) {
+    // Operands go straight from memory into the MFMA operand registers; there is no barrier in
+    // the K loop. The weights are the first operand and the token rows the second, so a lane's
+    // four results share one token row (lane & 15) and four consecutive weight rows
+    // 4 (lane >> 4) + i: the row's activation scale is one number per lane, loaded with its
+    // codes, and the weight block scale one number per wave.
+    const int kq = (lane >> 4) * 32;             // this lane's 32 K-bytes of a 128-wide block
+    const uint8_t* aptr[MT];
+    const float* asptr[MT];
 #pragma unroll
-        for (int i = 0; i < A_PER_THREAD; ++i) {
-            const int c = tid + i * THREADS;
-            aReg[i] = make_uint4(0, 0, 0, 0);
-            if (c < A_CHUNKS) {
-                const int src = sRow[c >> 3];
-                if (src >= 0)
-                    aReg[i] = *reinterpret_cast<const uint4*>(P.a + (int64_t)src * P.Kdim + kb * 128 + (c & 7) * 16);
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < (BM + THREADS - 1) / THREADS; ++i) {
-            const int r = tid + i * THREADS;
-            asReg[i] = 0.0f;
-            if (r < BM) {
-                const int src = sRow[r];
-                if (src >= 0) asReg[i] = P.as[(int64_t)src * KB + kb];
-            }
-        }
-    };
-    auto storeA = [&](int buf) {
-#pragma unroll
-        for (int i = 0; i < A_PER_THREAD; ++i) {
-            const int c = tid + i * THREADS;
-            if (c < A_CHUNKS) *reinterpret_cast<uint4*>(&sA[buf][(c >> 3) * kAPitch + (c & 7) * 16]) = aReg[i];
-        }
-#pragma unroll
-        for (int i = 0; i < (BM + THREADS - 1) / THREADS; ++i) {
-            const int r = tid + i * THREADS;
-            if (r < BM) sAs[buf][r] = asReg[i];
-        }
-    };
-
-    // ---- weight fragments, straight to registers
-    const int wcol0 = n0 + wn * NT * 16;        // first column of this wave (per tensor)
-    const int cblk = wcol0 / 128;                // its 128-row weight scale block
+    for (int mt = 0; mt < MT; ++mt) {
+        const int src = sRow[wm * MT * 16 + mt * 16 + (lane & 15)];
+        aptr[mt] = P.a + (int64_t)src * P.Kdim + kq;
+        asptr[mt] = P.as + (int64_t)src * KB;
+    }
+    const int wcol0 = n0 + wn * NT * 16;         // first column of this wave (per tensor)
     const bool wave_live = wcol0 < P.Ndim;
+    const int cblk = (wave_live ? wcol0 : 0) / 128;   // its 128-row weight scale block
     const uint8_t* W[2] = {P.w0, P.w1};
     const float* S[2] = {P.s0, P.s1};
-    auto loadB = [&](int kb, v8i (&dst)[NTEN][NT]) {
+    const uint8_t* bptr[NTEN][NT];
+    const float* swptr[NTEN];
+#pragma unroll
+    for (int ten = 0; ten < NTEN; ++ten) {
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+            int col = wcol0 + nt * 16 + (lane & 15);
+            col = col < P.Ndim ? col : P.Ndim - 1;   // columns past the end are never stored
+            bptr[ten][nt] = W[ten] + ((int64_t)e * P.Ndim + col) * P.Kdim + kq;
+        }
+        swptr[ten] = S[ten] + ((int64_t)e * NB128 + cblk) * KB;
+    }
+
+    struct Ops {
+        v8i a[MT];
+        float as[MT];
+        v8i b[NTEN][NT];
+        float sw[NTEN];   // weight block scales (uniform: scalar loads)
+    };
+    auto load = [&](int kb, Ops& o) {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            o.a[mt] = load_frag_global(aptr[mt] + kb * 128);
+            o.as[mt] = asptr[mt][kb];
+        }
 #pragma unroll
         for (int ten = 0; ten < NTEN; ++ten)
 #pragma unroll
-            for (int nt = 0; nt < NT; ++nt) {
-                const int col = wcol0 + nt * 16 + (lane & 15);
-                if (col < P.Ndim) {
-                    const uint8_t* ptr = W[ten] + ((int64_t)e * P.Ndim + col) * P.Kdim + kb * 128 + (lane >> 4) * 32;
-                    dst[ten][nt] = load_frag_global(ptr);
-                } else {
-                    dst[ten][nt] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
-                }
-            }
+            for (int nt = 0; nt < NT; ++nt) o.b[ten][nt] = load_frag_global(bptr[ten][nt] + kb * 128);
+#pragma unroll
+        for (int ten = 0; ten < NTEN; ++ten) o.sw[ten] = swptr[ten][kb];
     };
 
     v4f acc[NTEN][MT][NT];
@@ -179,126 +162,111 @@ __global__ __launch_bounds__(WM* WN * 64) void k_grouped_gemm(const GemmParams P
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) acc[ten][mt][nt] = v4f{0.f, 0.f, 0.f, 0.f};
 
-    v8i bCur[NTEN][NT], bNext[NTEN][NT];
-    loadA(0);
-    loadB(0, bCur);
-    storeA(0);
-    __syncthreads();
-
-    for (int kb = 0; kb < KB; ++kb) {
-        const int buf = kb & 1;
-        const bool more = kb + 1 < KB;
-        if (more) {
-            loadA(kb + 1);
-            loadB(kb + 1, bNext);
-        }
-        float sw[NTEN];
-#pragma unroll
-        for (int ten = 0; ten < NTEN; ++ten)
-            sw[ten] = wave_live ? S[ten][((int64_t)e * NB128 + cblk) * KB + kb] : 0.0f;
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-            const int rbase = wm * MT * 16 + mt * 16;
-            const v8i a = load_frag_lds(&sA[buf][(rbase + (lane & 15)) * kAPitch + (lane >> 4) * 32]);
-            float sa[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) sa[i] = sAs[buf][rbase + 4 * (lane >> 4) + i];
-#pragma unroll
-            for (int ten = 0; ten < NTEN; ++ten) {
-                float f[4];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) f[i] = sa[i] * sw[ten];
-#pragma unroll
-                for (int nt = 0; nt < NT; ++nt) {
-                    const v4f r = mfma_16x16x128_fp8(a, bCur[ten][nt]);
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) acc[ten][mt][nt][i] += f[i] * r[i];
-                }
-            }
-        }
-        if (more) storeA(buf ^ 1);
-        __syncthreads();
-        if (more) {
-#pragma unroll
-            for (int ten = 0; ten < NTEN; ++ten)
-#pragma unroll
-                for (int nt = 0; nt < NT; ++nt) bCur[ten][nt] = bNext[ten][nt];
-        }
-    }
-
-    if constexpr (MODE == 0) {
-        // h = silu(g) * u; per-row amax over the 128 columns of this workgroup
-        float h[MT][NT][4];
+    auto compute = [&](const Ops& o) {
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                float m = 0.0f;
+            for (int ten = 0; ten < NTEN; ++ten) {
+                const float f = o.as[mt] * o.sw[ten];
 #pragma unroll
                 for (int nt = 0; nt < NT; ++nt) {
+                    const v4f r = mfma_16x16x128_fp8(o.b[ten][nt], o.a[mt]);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) acc[ten][mt][nt][i] += f * r[i];
+                }
+            }
+    };
+
+    // two register sets in turn: while one block is multiplied, the next is loading. The loads
+    // are unconditional (past the end they repeat the last block, unused), so that no set is
+    // ever copied -- a copy would wait for the loads in flight -- and the scheduling barriers
+    // keep each set's loads after the matrix ops that read it.
+    Ops X, Y;
+    load(0, X);
+    for (int kb = 0; kb < KB; kb += 2) {
+        load(kb + 1 < KB ? kb + 1 : KB - 1, Y);
+        compute(X);
+        __builtin_amdgcn_sched_barrier(0);
+        load(kb + 2 < KB ? kb + 2 : KB - 1, X);
+        if (kb + 1 < KB) compute(Y);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+
+    // acc[ten][mt][nt][i]: token row wm MT 16 + 16 mt + (lane & 15) of the tile, column
+    // wcol0 + 16 nt + 4 (lane >> 4) + i
+    if constexpr (MODE == 0) {
+        // h = silu(g) * u; per-row amax over the workgroup's 128 columns (lane groups, then waves)
+        float h[MT][NT * 4];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            float m = 0.0f;
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
                     const float v = silu_fast(acc[0][mt][nt][i]) * acc[1][mt][nt][i];
-                    h[mt][nt][i] = v;
+                    h[mt][nt * 4 + i] = v;
                     m = __builtin_fmaxf(m, __builtin_fabsf(v));
                 }
-#pragma unroll
-                for (int msk = 8; msk >= 1; msk >>= 1) m = __builtin_fmaxf(m, __shfl_xor(m, msk, 16));
-                if ((lane & 15) == 0) sRed[wn][wm * MT * 16 + mt * 16 + 4 * (lane >> 4) + i] = m;
-            }
+            m = __builtin_fmaxf(m, __shfl_xor(m, 16));
+            m = __builtin_fmaxf(m, __shfl_xor(m, 32));
+            if ((lane >> 4) == 0) sRed[wn][wm * MT * 16 + mt * 16 + lane] = m;
+        }
         __syncthreads();
         const int dff = P.Ndim;
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
+        for (int mt = 0; mt < MT; ++mt) {
+            const int row = wm * MT * 16 + mt * 16 + (lane & 15);
+            float amax = 0.0f;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int row = wm * MT * 16 + mt * 16 + 4 * (lane >> 4) + i;
-                float amax = 0.0f;
+            for (int w = 0; w < WN; ++w) amax = __builtin_fmaxf(amax, sRed[w][row]);
+            const float sc = group_scale(amax);
+            scale_group(h[mt], sc);
+            if (row < nrows) {
+                const int64_t p = p0 + row;
 #pragma unroll
-                for (int w = 0; w < WN; ++w) amax = __builtin_fmaxf(amax, sRed[w][row]);
-                const float sc = group_scale(amax);
-                float q[NT];
-#pragma unroll
-                for (int nt = 0; nt < NT; ++nt) q[nt] = h[mt][nt][i];
-                scale_group(q, sc);
-                if (row < nrows) {
-                    const int64_t p = p0 + row;
-#pragma unroll
-                    for (int nt = 0; nt < NT; ++nt) {
-                        const int col = wcol0 + nt * 16 + (lane & 15);
-                        P.hq[p * dff + col] = (uint8_t)f32x2_to_e4m3(q[nt], 0.0f);
-                    }
-                    if (wn == 0 && (lane & 15) == 0) P.hs[p * (dff / 128) + n0 / 128] = sc;
+                for (int nt = 0; nt < NT; ++nt) {
+                    const uint32_t lo = f32x2_to_e4m3(h[mt][nt * 4], h[mt][nt * 4 + 1]);
+                    const uint32_t hi = f32x2_to_e4m3(h[mt][nt * 4 + 2], h[mt][nt * 4 + 3]);
+                    *reinterpret_cast<uint32_t*>(P.hq + p * dff + wcol0 + nt * 16 + 4 * (lane >> 4)) = lo | (hi << 16);
                 }
+                if (wn == 0 && (lane >> 4) == 0) P.hs[p * (dff / 128) + n0 / 128] = sc;
             }
+        }
     } else {
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
+        for (int mt = 0; mt < MT; ++mt) {
+            const int row = wm * MT * 16 + mt * 16 + (lane & 15);
+            if (row >= nrows) continue;
+            const int64_t p = p0 + row;
+            int64_t dst = p;
+            float wgt = 1.0f;
+            if (P.scatter) {   // top-1 combine: bf16(0 + w * bf16(y)), the combine's arithmetic
+                dst = P.scatter[p];
+                if (dst < 0 || dst >= P.out_rows) continue;
+                wgt = P.scatter_w[dst];
+            }
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int row = wm * MT * 16 + mt * 16 + 4 * (lane >> 4) + i;
-                if (row < nrows) {
-                    const int64_t p = p0 + row;
-                    int64_t dst = p;
-                    float wgt = 1.0f;
-                    if (P.scatter) {   // top-1 combine: bf16(0 + w * bf16(y)), the combine's arithmetic
-                        dst = P.scatter[p];
-                        if (dst < 0 || dst >= P.out_rows) continue;
-                        wgt = P.scatter_w[dst];
-                    }
+            for (int nt = 0; nt < NT; ++nt) {
+                const int col = wcol0 + nt * 16 + 4 * (lane >> 4);
+                if (col < P.Ndim) {   // Ndim is a multiple of 128: the 4 columns are all in range
+                    uint32_t v[4];
 #pragma unroll
-                    for (int nt = 0; nt < NT; ++nt) {
-                        const int col = wcol0 + nt * 16 + (lane & 15);
-                        if (col < P.Ndim) {
-                            uint32_t v = f32_to_bf16(acc[0][mt][nt][i]);
-                            if (P.scatter) {
-                                float c = 0.0f;
-                                c += wgt * bf16_to_f32(v);
-                                v = f32_to_bf16(c);
-                            }
-                            P.y[dst * P.Ndim + col] = (uint16_t)v;
+                    for (int i = 0; i < 4; ++i) {
+                        v[i] = f32_to_bf16(acc[0][mt][nt][i]);
+                        if (P.scatter) {
+                            float c = 0.0f;
+                            c += wgt * bf16_to_f32(v[i]);
+                            v[i] = f32_to_bf16(c);
                         }
                     }
+                    uint2 o;
+                    o.x = v[0] | (v[1] << 16);
+                    o.y = v[2] | (v[3] << 16);
+                    *reinterpret_cast<uint2*>(P.y + dst * P.Ndim + col) = o;
                 }
             }
+        }
     }
 }
 

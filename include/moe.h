@@ -261,7 +261,11 @@ int moe_last_hip_error(void);
  * launch of the library's kernels, for measuring the kernels inside a larger
  * timed region. Off by default. Kinds: MOE_KERNEL_*. moe_profile_read waits
  * for the recorded events, adds their elapsed times to the totals and returns
- * the totals since the last reset: summed milliseconds and launch count. */
+ * the totals since the last reset: summed milliseconds and launch count.
+ * MOE_KERNEL_QUANT times the activation quantisation launch of moe_grouped_swiglu
+ * and moe_grouped_swiglu_top1, which also builds the GEMM tile list;
+ * MOE_KERNEL_DISPATCH times moe_dispatch and, in moe_grouped_swiglu_q, the tile
+ * list's own launch. */
 enum {
     MOE_KERNEL_QUANT = 0,
     MOE_KERNEL_DISPATCH = 1,

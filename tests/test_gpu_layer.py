@@ -56,6 +56,38 @@ def test_tiny_k2_with_shared_expert():
     _check_small(Config("tiny_k2", 32, 256, 384, 16, 4, "rmsnorm", "uniform", "uniform", True, seed=11))
 
 
+def test_shared_expert_stream_matches_one_stream():
+    """moe_layer runs the shared expert on a second stream; the result must be bit-identical to
+    the same calls made one after another on one stream (dispatch, routed experts, shared
+    expert, combine), at every tile height, and stay so when the caller's stream is not the
+    default one."""
+    cfg = Config("side_stream", 300, 256, 384, 6, 3, "rmsnorm", "uniform", "uniform", True, seed=31)
+    x_bits = make_x_bits(cfg)
+    ids, w = make_routing(cfg)
+    exd = experts_dev(make_experts_host(cfg))
+    shd = experts_dev(make_shared_host(cfg))
+    x = bf16_dev(x_bits)
+    t_ids = torch.from_numpy(ids).cuda()
+    t_w = torch.from_numpy(w).cuda()
+    for shape in ("auto", "16", "128", "224"):
+        flags = 0 if shape == "auto" else SHAPES[shape]
+        say(f"shared expert on a second stream, shape={shape}")
+        disp = moe.dispatch(t_ids, cfg.E)
+        y = moe.grouped_swiglu(x, disp, exd, flags)
+        sh = moe.grouped_swiglu(x, moe.identity_dispatch(cfg.N, x.device), shd)
+        one = bits_host(moe.combine(y, disp, t_w, sh))
+        two = bits_host(moe.moe_layer(x, t_ids, t_w, exd, shd, flags=flags))
+        torch.cuda.synchronize()
+        assert np.array_equal(one, two), f"shape {shape}: two-stream result differs"
+        caller = torch.cuda.Stream()
+        caller.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(caller):
+            three = moe.moe_layer(x, t_ids, t_w, exd, shd, flags=flags)
+        torch.cuda.current_stream().wait_stream(caller)
+        torch.cuda.synchronize()
+        assert np.array_equal(bits_host(three), one), f"shape {shape}: result on a caller stream differs"
+
+
 def test_ragged_dims():
     # d = 384: the down kernel's last 256-column block is half empty; 77 tokens: ragged tiles.
     # d_ff = 1024 keeps enough requantisation groups per row that the matrix cores' own

@@ -275,6 +275,10 @@ enum {
     MOE_KERNEL_KINDS = 5
 };
 moe_status moe_profile_enable(int on);
+/* Times only the kinds whose bit (1 << MOE_KERNEL_*) is set in kind_mask (0: none). Each timed
+ * launch adds two event records to its stream, so a measurement that needs one kind's times
+ * can leave the other launches uninstrumented. Bits above the last kind: MOE_ERR_SHAPE. */
+moe_status moe_profile_enable_kinds(uint32_t kind_mask);
 moe_status moe_profile_reset(void);
 moe_status moe_profile_read(int kind, double* total_ms, int64_t* launches);
 

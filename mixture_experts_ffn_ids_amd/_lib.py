@@ -77,6 +77,8 @@ def _lib_handle():
         lib.moe_quantize_rows.argtypes = [P, i64, i32, P, P, P]
         lib.moe_profile_enable.restype = st
         lib.moe_profile_enable.argtypes = [ctypes.c_int]
+        lib.moe_profile_enable_kinds.restype = st
+        lib.moe_profile_enable_kinds.argtypes = [ctypes.c_uint32]
         lib.moe_profile_reset.restype = st
         lib.moe_profile_reset.argtypes = []
         lib.moe_profile_read.restype = st

@@ -353,8 +353,15 @@ def dense_block_ffn(hidden: torch.Tensor, gain: torch.Tensor, eps: float, mlp, f
 
 
 # ---------------------------------------------------------------- profiling
-def profile_enable(on: bool = True):
-    check(lib().moe_profile_enable(1 if on else 0), "moe_profile_enable")
+def profile_enable(on: bool = True, kinds=None):
+    """Time every kernel kind (on), none (off), or only the given KERNEL_* kinds."""
+    if kinds is None or not on:
+        check(lib().moe_profile_enable(1 if on else 0), "moe_profile_enable")
+    else:
+        mask = 0
+        for k in kinds:
+            mask |= 1 << int(k)
+        check(lib().moe_profile_enable_kinds(mask), "moe_profile_enable_kinds")
 
 
 def profile_reset():

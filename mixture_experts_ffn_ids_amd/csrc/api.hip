@@ -54,7 +54,7 @@ struct Pending {
     hipEvent_t a, b;
 };
 std::mutex g_prof_mu;
-bool g_prof_on = false;
+uint32_t g_prof_mask = 0;   // bit k: launches of kind k are timed
 std::vector<hipEvent_t> g_prof_pool;
 std::vector<Pending> g_prof_pending;
 double g_prof_ms[MOE_KERNEL_KINDS] = {0};
@@ -76,7 +76,7 @@ class ProfScope {
 public:
     ProfScope(int kind, hipStream_t s) : kind_(kind), s_(s) {
         std::lock_guard<std::mutex> lk(g_prof_mu);
-        if (!g_prof_on) return;
+        if (kind < 0 || kind >= MOE_KERNEL_KINDS || !((g_prof_mask >> kind) & 1u)) return;
         a_ = prof_event();
         b_ = prof_event();
         if (!a_ || !b_ || hipEventRecord(a_, s_) != hipSuccess) release();
@@ -406,7 +406,14 @@ moe_status moe_rmsnorm_quantize_rows(const uint16_t* h, const uint16_t* gain, fl
 
 moe_status moe_profile_enable(int on) {
     std::lock_guard<std::mutex> lk(g_prof_mu);
-    g_prof_on = on != 0;
+    g_prof_mask = on != 0 ? (1u << MOE_KERNEL_KINDS) - 1u : 0u;
+    return MOE_OK;
+}
+
+moe_status moe_profile_enable_kinds(uint32_t kind_mask) {
+    if (kind_mask >> MOE_KERNEL_KINDS) return MOE_ERR_SHAPE;
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    g_prof_mask = kind_mask;
     return MOE_OK;
 }
 

@@ -117,6 +117,9 @@ def test_profile_api_without_gpu():
     n = ctypes.c_int64()
     assert L.moe_profile_read(99, ctypes.byref(ms), ctypes.byref(n)) == 2
     assert L.moe_profile_read(0, ctypes.byref(ms), ctypes.byref(n)) == 0 and n.value == 0
+    assert L.moe_profile_enable_kinds(1 << 5) == 2          # no such kind
+    assert L.moe_profile_enable_kinds(1 << 2) == 0
+    assert L.moe_profile_enable(0) == 0
 
 
 def test_fused_neighbour_calls_validate_on_host():

@@ -217,3 +217,35 @@ def test_activation_offsets_beyond_32_bits():
     say(f"offsets64 oracle tokens={len(tok)}")
     _, ref64 = oracle.moe_forward(x_tok, ids[tok], w[tok], exh)
     assert_layer_close(outs[0], ref64, "offsets64 sampled")
+
+
+def test_profiler_times_only_the_selected_kinds():
+    """moe_profile_enable_kinds: with only gate|up selected, a layer call records one gate|up
+    launch and nothing for the other kinds; with every kind selected, each kind is counted."""
+    cfg = CONFIGS[0]
+    x = bf16_dev(make_x_bits(cfg))
+    ids, w = make_routing(cfg)
+    exd = experts_dev(make_experts_host(cfg))
+    t_ids = torch.from_numpy(ids).cuda()
+    t_w = torch.from_numpy(w).cuda()
+    kinds = (moe.KERNEL_QUANT, moe.KERNEL_DISPATCH, moe.KERNEL_GATE_UP, moe.KERNEL_DOWN, moe.KERNEL_COMBINE)
+    try:
+        moe.profile_reset()
+        moe.profile_enable(True, kinds=[moe.KERNEL_GATE_UP])
+        moe.moe_layer(x, t_ids, t_w, exd)
+        torch.cuda.synchronize()
+        moe.profile_enable(False)
+        counts = {k: moe.profile_read(k)[1] for k in kinds}
+        assert counts[moe.KERNEL_GATE_UP] == 1
+        assert all(counts[k] == 0 for k in kinds if k != moe.KERNEL_GATE_UP), counts
+        moe.profile_reset()
+        moe.profile_enable(True)
+        moe.moe_layer(x, t_ids, t_w, exd)
+        torch.cuda.synchronize()
+        moe.profile_enable(False)
+        counts = {k: moe.profile_read(k)[1] for k in kinds}
+        assert all(counts[k] >= 1 for k in kinds), counts
+        assert moe.profile_read(moe.KERNEL_GATE_UP)[0] > 0.0
+    finally:
+        moe.profile_enable(False)
+        moe.profile_reset()

@@ -3,11 +3,24 @@
 //
 // Memory-bound: each group of 16 lanes owns 128-value groups; a lane loads 8 bf16
 // (16 B) of a group, the group's largest magnitude is reduced across the 16 lanes
-// with xor shuffles, then every lane divides by the scale (IEEE division) and stores
-// 8 codes (8 B).
+// with xor shuffles, then every lane divides by the scale (the IEEE quotient, by a
+// correction of the product with the reciprocal) and stores 8 codes (8 B).
 #include "moe_internal.h"
 
 namespace moe {
+
+// v / s rounded to nearest even in binary32, the IEEE quotient, from r = 1/s (itself the
+// IEEE quotient): q = v r is within an ulp of v / s, the fused multiply-add gives the remainder
+// v - q s, and q + (v - q s) r rounded once is the correctly rounded quotient (Markstein's
+// correction). Two fused multiply-adds per value instead of a full division; the caller keeps
+// s >= 2^-100, so that neither the remainder nor its product with r underflows. A zero result
+// takes q's sign (that of v), as the division would.
+__device__ __forceinline__ float div_by_scale(float v, float s, float r) {
+    const float q = v * r;
+    const float rem = __builtin_fmaf(-q, s, v);
+    const float out = __builtin_fmaf(rem, r, q);
+    return out == 0.0f ? q : out;
+}
 
 // One 128-value group: lane `sub` of its 16 holds values 8 sub .. 8 sub + 7 in raw.
 __device__ __forceinline__ void quant_group(const uint4 raw, uint2& codes, float& scale) {
@@ -22,8 +35,17 @@ __device__ __forceinline__ void quant_group(const uint4 raw, uint2& codes, float
 #pragma unroll
     for (int m = 8; m >= 1; m >>= 1) amax = __builtin_fmaxf(amax, __shfl_xor(amax, m, 16));
     const float sc = group_scale(amax);
-    codes.x = f32x2_to_e4m3(v[0] / sc, v[1] / sc) | (f32x2_to_e4m3(v[2] / sc, v[3] / sc) << 16);
-    codes.y = f32x2_to_e4m3(v[4] / sc, v[5] / sc) | (f32x2_to_e4m3(v[6] / sc, v[7] / sc) << 16);
+    float q[8];
+    if (sc >= 0x1p-100f) {
+        const float r = 1.0f / sc;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) q[i] = div_by_scale(v[i], sc, r);
+    } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) q[i] = v[i] / sc;
+    }
+    codes.x = f32x2_to_e4m3(q[0], q[1]) | (f32x2_to_e4m3(q[2], q[3]) << 16);
+    codes.y = f32x2_to_e4m3(q[4], q[5]) | (f32x2_to_e4m3(q[6], q[7]) << 16);
     scale = sc;
 }
 

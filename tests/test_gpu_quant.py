@@ -54,3 +54,33 @@ def test_e4m3_conversion_exhaustive_over_bf16():
     assert np.all(s_ref == 1.0)
     assert np.array_equal(s.cpu().numpy(), s_ref)
     assert np.array_equal(q.cpu().numpy(), q_ref)
+
+
+@pytest.mark.parametrize("amax_bits", [0x3F80, 0x3FFF, 0x43E0, 0x4000, 0x7F7F, 0x0080, 0x3DCD, 0x1C01, 0x6A5A, 0x0D80],
+                         ids=lambda b: f"amax{b:04x}")
+def test_quantize_every_bf16_value_against_one_scale(amax_bits):
+    """Every finite bf16 value of magnitude at most amax, in groups whose largest magnitude is
+    amax: the codes (the quotient v / s rounded by the kernel's corrected reciprocal product, or
+    by a plain division for tiny scales) must equal the oracle's, which divides. The amax values
+    include scales whose reciprocals are inexact, the largest and smallest normal bf16 and
+    scales below 2^-100."""
+    allb = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    f32 = (allb.astype(np.uint32) << 16).view(np.float32)
+    amax = np.array([amax_bits << 16], np.uint32).view(np.float32)[0]
+    keep = np.isfinite(f32) & (np.abs(f32) <= amax)
+    v = allb[keep]
+    per = 127
+    groups = (v.size + per - 1) // per
+    pad = groups * per - v.size
+    v = np.concatenate([v, np.zeros(pad, np.uint16)]).reshape(groups, per)
+    col = np.full((groups, 1), amax_bits, np.uint16)
+    bits = np.concatenate([col, v], axis=1)                    # [groups, 128], first value = amax
+    if groups % 8:                                             # 8 groups per row of 1024
+        bits = np.concatenate([bits, np.tile(bits[:1], (8 - groups % 8, 1))])
+    bits = np.ascontiguousarray(bits.reshape(-1, 1024))
+    say(f"quantize every bf16 value, amax bits {amax_bits:#06x}, {bits.shape[0]} rows")
+    q, s = moe.quantize_rows(bf16_dev(bits))
+    torch.cuda.synchronize()
+    q_ref, s_ref = oracle.quant_rows_bf16(bits)
+    assert np.array_equal(s.cpu().numpy().view(np.uint32), s_ref.view(np.uint32))
+    assert np.array_equal(q.cpu().numpy(), q_ref)

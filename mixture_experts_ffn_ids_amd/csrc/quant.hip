@@ -13,8 +13,8 @@ namespace moe {
 // IEEE quotient): q = v r is within an ulp of v / s, the fused multiply-add gives the remainder
 // v - q s, and q + (v - q s) r rounded once is the correctly rounded quotient (Markstein's
 // correction). Two fused multiply-adds per value instead of a full division; the caller keeps
-// s >= 2^-100, so that neither the remainder nor its product with r underflows. A zero result
-// takes q's sign (that of v), as the division would.
+// s finite and >= 2^-100, so that neither the remainder nor its product with r underflows. A
+// zero result takes q's sign (that of v), as the division would.
 __device__ __forceinline__ float div_by_scale(float v, float s, float r) {
     const float q = v * r;
     const float rem = __builtin_fmaf(-q, s, v);
@@ -36,7 +36,7 @@ __device__ __forceinline__ void quant_group(const uint4 raw, uint2& codes, float
     for (int m = 8; m >= 1; m >>= 1) amax = __builtin_fmaxf(amax, __shfl_xor(amax, m, 16));
     const float sc = group_scale(amax);
     float q[8];
-    if (sc >= 0x1p-100f) {
+    if (sc >= 0x1p-100f && sc <= 0x1.fffffep127f) {   // an infinite amax divides, as before
         const float r = 1.0f / sc;
 #pragma unroll
         for (int i = 0; i < 8; ++i) q[i] = div_by_scale(v[i], sc, r);

@@ -84,3 +84,19 @@ def test_quantize_every_bf16_value_against_one_scale(amax_bits):
     q_ref, s_ref = oracle.quant_rows_bf16(bits)
     assert np.array_equal(s.cpu().numpy().view(np.uint32), s_ref.view(np.uint32))
     assert np.array_equal(q.cpu().numpy(), q_ref)
+
+
+def test_group_with_an_infinity_keeps_finite_codes():
+    """A group whose largest magnitude is infinite gets an infinite scale and every finite value
+    the code of a signed zero, as the oracle's division gives (the infinite element's own code is
+    not compared: the format has no infinity). The other group of the row is unaffected."""
+    x = np.linspace(-3, 3, 256, dtype=np.float32).reshape(1, 256)
+    x[0, 5] = np.inf
+    bits = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    say("quantize a group holding an infinity")
+    q, s = moe.quantize_rows(bf16_dev(bits))
+    torch.cuda.synchronize()
+    q_ref, s_ref = oracle.quant_rows_bf16(bits)
+    assert np.array_equal(s.cpu().numpy().view(np.uint32), s_ref.view(np.uint32))
+    finite = np.isfinite(x)
+    assert np.array_equal(q.cpu().numpy()[finite], q_ref[finite])

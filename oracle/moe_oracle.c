@@ -131,9 +131,12 @@ uint16_t orc_bf16_from_double(double v)
 /* ---------------------------------------------------------------------
  * Dynamic quantisation of a row to e4m3 with one float32 scale per
  * 128-element group: scale = amax / 448, code = e4m3(v / scale); an all-zero
- * group gets scale 1 and zero codes.
+ * group gets scale 1, so its codes are the (signed) zeros.
  * ("Input features" page, evidence "linear": activation_scheme dynamic,
- * fmt e4m3.)
+ * fmt e4m3.) The pages do not speak of NaN. Reading taken: a NaN has no
+ * magnitude, so amax is taken over the other values (a NaN never passes the
+ * comparison below), and a NaN value is encoded like any other, as the NaN
+ * code (v / scale is NaN).
  * ------------------------------------------------------------------- */
 static void quant_group_f32(const float* v, int n, uint8_t* q, float* s)
 {
@@ -143,13 +146,7 @@ static void quant_group_f32(const float* v, int n, uint8_t* q, float* s)
         if (a > amax)
             amax = a;
     }
-    if (amax == 0.0f) {
-        *s = 1.0f;
-        for (int i = 0; i < n; ++i)
-            q[i] = signbit(v[i]) ? 0x80 : 0x00;
-        return;
-    }
-    float scale = amax / E4M3_MAX;
+    float scale = amax > 0.0f ? amax / E4M3_MAX : 1.0f;
     *s = scale;
     for (int i = 0; i < n; ++i) {
         float t = v[i] / scale;

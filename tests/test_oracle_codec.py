@@ -122,3 +122,30 @@ def test_quantiser_properties():
 def test_quantiser_rejects_bad_width():
     with pytest.raises(oracle.OracleError):
         oracle.quant_rows_f32(np.zeros((2, 100), np.float32))
+
+
+def test_quantiser_nan_reading_against_library_codec():
+    """The pages do not speak of NaN; the reading taken is that a NaN has no magnitude (the group
+    scale comes from the other values) and is encoded as the NaN code. Pinned against torch's
+    codec: scales and the other values' codes equal the torch-op quantiser's on the same rows with
+    the NaNs replaced by zeros, and every NaN gets torch's float8_e4m3fn code of NaN. A group of
+    NaNs and zeros only has scale 1."""
+    rng = np.random.default_rng(17)
+    x = (rng.standard_normal((8, 512)) * np.exp2(rng.integers(-6, 6, (8, 1)))).astype(np.float32)
+    x[0, 7] = np.nan
+    x[1, ::3] = np.nan
+    x[2, :128] = np.nan
+    x[3, 128:256] = 0.0
+    x[3, 130] = np.nan
+    x[4, 300] = -np.nan
+    q, s = oracle.quant_rows_f32(x)
+    nan = np.isnan(x)
+    clean = torch.from_numpy(np.where(nan, np.float32(0.0), x)).reshape(8, 4, 128)
+    amax = clean.abs().amax(-1)
+    s_ref = torch.where(amax > 0, amax / 448.0, torch.ones_like(amax))
+    q_ref = (clean / s_ref[..., None]).to(torch.float8_e4m3fn).view(torch.uint8).reshape(8, 512).numpy()
+    assert np.array_equal(s, s_ref.numpy())
+    assert np.array_equal(q[~nan], q_ref[~nan])
+    nan_code = torch.tensor([float("nan")]).to(torch.float8_e4m3fn).view(torch.uint8).item()
+    assert (q[nan] & 0x7F == nan_code & 0x7F).all()
+    assert s[2, 0] == 1.0 and s[3, 1] == 1.0

@@ -242,3 +242,32 @@ def test_oracle_rejects_bad_ids():
     dup[4, 1] = dup[4, 0]
     with pytest.raises(oracle.OracleError):
         oracle.moe_forward(x, dup, w, ex)
+
+
+def test_expert_rows_against_library_mlp():
+    """oracle.expert_rows evaluates one expert on one token per row. Pinned against the torch
+    library MLP above (F.linear / F.silu on dequantised weights, float8_e4m3fn activation
+    quantisation) for (token, expert) pairs in a scrambled order, with repeats, the last token
+    and the last expert: y to 1e-9 relative, and the requantised product h (codes and scales)
+    equal to the pinned quantiser applied to torch's float32 h. A wrong token index, expert
+    offset or row stride fails it."""
+    cfg = Config("rows", 24, 384, 256, 6, 2, "normal", "uniform", "uniform", False, seed=23)
+    x = make_x_bits(cfg)
+    ex = make_experts_host(cfg)
+    rng = np.random.default_rng(24)
+    tokens = rng.integers(0, cfg.N, 13)
+    experts = rng.integers(0, cfg.E, 13)
+    tokens = np.concatenate([tokens, [cfg.N - 1, 0, cfg.N - 1, tokens[0]]]).astype(np.int64)
+    experts = np.concatenate([experts, [cfg.E - 1, cfg.E - 1, 0, experts[0]]]).astype(np.int32)
+    y, hq, hs = oracle.expert_rows(x, ex, tokens, experts)
+    xt = _torch_quant(torch.from_numpy(oracle.bf16_to_f32(x).copy()))
+    for i, (t, e) in enumerate(zip(tokens, experts)):
+        ref = _mlp(xt[t:t + 1], ex, int(e)).numpy()[0]
+        assert np.abs(y[i] - ref).max() <= 1e-9 * np.abs(ref).max()
+        g = F.linear(xt[t:t + 1], _dequant_w(ex.w_gate[e], ex.s_gate[e]))
+        u = F.linear(xt[t:t + 1], _dequant_w(ex.w_up[e], ex.s_up[e]))
+        h = (F.silu(g) * u).to(torch.float32).numpy()
+        q_ref, s_ref = oracle.quant_rows_f32(h)
+        assert np.array_equal(hq[i], q_ref[0]) and np.array_equal(hs[i], s_ref[0])
+    # the same pair gives the same row wherever it appears
+    assert np.array_equal(y[0], y[16]) and np.array_equal(hq[0], hq[16])

@@ -58,3 +58,48 @@ def assert_layer_close(gpu_bits: np.ndarray, ref64: np.ndarray, what: str = ""):
     print(f"[parity] {what}: max per-token rel L2 {rel:.3e}, max elementwise err/max|ref| {elem:.3e}", flush=True)
     assert rel <= REL_L2_TOL, f"{what}: per-token relative L2 {rel} > {REL_L2_TOL}"
     assert elem <= ELEM_TOL, f"{what}: elementwise error {elem} > {ELEM_TOL} * max|ref|"
+
+
+class WholeBatch:
+    """Whole-batch comparison against the oracle, fed chunk by chunk so that the oracle's
+    float64 result never has to be held for the whole batch: per-token relative L2 for every
+    token, and the elementwise bar against the largest |ref| over the whole batch."""
+
+    def __init__(self, what: str, n: int):
+        self.what = what
+        self.rel = np.zeros(n, np.float64)
+        self.max_diff = 0.0
+        self.max_ref = 0.0
+        self.done = 0
+
+    def add(self, rows: np.ndarray, gpu_bits: np.ndarray, ref64: np.ndarray):
+        g = oracle.bf16_to_f32(gpu_bits).astype(np.float64)
+        assert np.all(np.isfinite(g)), f"{self.what}: non-finite output"
+        r = np.asarray(ref64, dtype=np.float64)
+        diff = g - r
+        num = np.sqrt((diff ** 2).sum(axis=1))
+        den = np.sqrt((r ** 2).sum(axis=1))
+        self.rel[rows] = np.where(den > 0, num / np.where(den > 0, den, 1.0), num)
+        self.max_diff = max(self.max_diff, float(np.abs(diff).max()) if diff.size else 0.0)
+        self.max_ref = max(self.max_ref, float(np.abs(r).max()) if r.size else 0.0)
+        self.done += len(rows)
+
+    def summary(self) -> dict:
+        n = self.rel.size
+        worst = int(self.rel.argmax()) if n else -1
+        elem = self.max_diff / self.max_ref if self.max_ref > 0 else self.max_diff
+        return {"tokens": n, "max_rel_l2": float(self.rel.max()) if n else 0.0,
+                "p99_9_rel_l2": float(np.quantile(self.rel, 0.999)) if n else 0.0,
+                "median_rel_l2": float(np.median(self.rel)) if n else 0.0,
+                "worst_token": worst, "elem_err_over_max_ref": float(elem),
+                "tokens_above_half_bar": int((self.rel > REL_L2_TOL / 2).sum())}
+
+    def check(self):
+        assert self.done == self.rel.size, f"{self.what}: {self.done} of {self.rel.size} tokens compared"
+        s = self.summary()
+        print(f"[whole-batch] {self.what}: " + " ".join(f"{k}={v:.3e}" if isinstance(v, float) else f"{k}={v}"
+                                                     for k, v in s.items()), flush=True)
+        assert s["max_rel_l2"] <= REL_L2_TOL, f"{self.what}: per-token relative L2 {s['max_rel_l2']} > {REL_L2_TOL}"
+        assert s["elem_err_over_max_ref"] <= ELEM_TOL, \
+            f"{self.what}: elementwise error {s['elem_err_over_max_ref']} > {ELEM_TOL} * max|ref|"
+        return s

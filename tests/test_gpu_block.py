@@ -12,9 +12,8 @@ import torch
 import mixture_experts_ffn_ids_amd as moe
 import oracle
 from parity import assert_layer_close, bf16_dev, bits_host, experts_dev, say
-from workloads import Config, config_by_name, make_routing
-from workloads.gen import experts_to_host, make_block_inputs, make_experts_device, make_experts_host, \
-    make_shared_device, make_shared_host
+from workloads import Config, make_routing
+from workloads.gen import make_block_inputs, make_experts_host, make_shared_host
 
 pytestmark = pytest.mark.gpu
 
@@ -112,23 +111,3 @@ def test_combine_residual_zero_weights_returns_residual():
     out = moe.combine(y, disp, torch.zeros_like(torch.from_numpy(w)).cuda(), residual=h)
     torch.cuda.synchronize()
     assert np.array_equal(bits_host(out), h_bits)
-
-
-def test_block_ffn_full_size_prefill():
-    """The fused block path at the 8192-token prefill shapes; outputs on sampled tokens."""
-    cfg = config_by_name("k2_prefill_8192")
-    h_bits, g_bits = make_block_inputs(cfg)
-    ids, w = make_routing(cfg)
-    say("block prefill weights")
-    exd = make_experts_device(cfg)
-    say("block prefill layer")
-    out = moe.moe_block_ffn(bf16_dev(h_bits), bf16_dev(g_bits), EPS, torch.from_numpy(ids).cuda(),
-                            torch.from_numpy(w).cuda(), exd)
-    torch.cuda.synchronize()
-    out_bits = bits_host(out)
-    tok = np.array([0, 1, 4095, 6000, cfg.N - 1], np.int64)
-    exh = experts_to_host(exd, np.unique(ids[tok]))
-    say("block prefill oracle")
-    x_norm = oracle.rmsnorm_rows(h_bits[tok], g_bits, EPS)
-    _, ref64 = oracle.moe_forward(x_norm, ids[tok], w[tok], exh, residual=h_bits[tok])
-    assert_layer_close(out_bits[tok], ref64, "block prefill sampled")

@@ -9,8 +9,7 @@ import mixture_experts_ffn_ids_amd as moe
 import oracle
 from parity import assert_layer_close, bf16_dev, bits_host, experts_dev, say
 from workloads import CONFIGS, Config, make_routing, make_x_bits
-from workloads.gen import HostExperts, experts_to_host, make_experts_device, make_experts_host, \
-    make_shared_device, make_shared_host
+from workloads.gen import make_experts_host, make_shared_host
 
 pytestmark = pytest.mark.gpu
 
@@ -135,47 +134,6 @@ def test_zero_input_gives_zero_output():
     say("layer zero input")
     out = _layer(np.zeros((cfg.N, cfg.d), np.uint16), ids, w, exd)
     assert np.all(oracle.bf16_to_f32(out) == 0.0)
-
-
-# --------------------------------------------------------------------------- K2 shapes
-_SAMPLE = 12
-
-
-def _sample_tokens(cfg, ids):
-    rng = np.random.default_rng(99)
-    sel = {0, cfg.N - 1}
-    sel.update(int(t) for t in rng.choice(cfg.N, size=min(cfg.N, _SAMPLE), replace=False))
-    if cfg.ids_mode == "zipf":
-        hot = np.bincount(ids.ravel(), minlength=cfg.E).argmax()
-        sel.update(int(t) for t in np.nonzero((ids == hot).any(1))[0][:4])
-    return np.array(sorted(sel), np.int64)
-
-
-@pytest.mark.parametrize("cfg", CONFIGS[1:], ids=[c.name for c in CONFIGS[1:]])
-def test_k2_config_full_size(cfg):
-    """The full-size layer in the launch configuration the benchmark times (automatic tile
-    shape); dispatch compared on every slot, outputs on sampled tokens."""
-    x = make_x_bits(cfg)
-    ids, w = make_routing(cfg)
-    say(f"k2 weights {cfg.name}")
-    exd = make_experts_device(cfg)
-    shd = make_shared_device(cfg) if cfg.shared else None
-    say(f"k2 layer {cfg.name}")
-    out = _layer(x, ids, w, exd, shd)
-    out2 = _layer(x, ids, w, exd, shd)
-    assert np.array_equal(out, out2), "two runs differ"
-    assert np.all(np.isfinite(oracle.bf16_to_f32(out)))
-    d = moe.dispatch(torch.from_numpy(ids).cuda(), cfg.E)
-    c, o, ss, sp = oracle.dispatch(ids, cfg.E)
-    assert np.array_equal(d.counts.cpu().numpy(), c) and np.array_equal(d.offsets.cpu().numpy(), o)
-    assert np.array_equal(d.sorted_slot.cpu().numpy(), ss) and np.array_equal(d.slot_pos.cpu().numpy(), sp)
-    tok = _sample_tokens(cfg, ids)
-    need = np.unique(ids[tok])
-    say(f"k2 oracle {cfg.name} tokens={len(tok)} experts={len(need)}")
-    exh = experts_to_host(exd, need)
-    shh = experts_to_host(shd) if shd is not None else None
-    _, ref64 = oracle.moe_forward(x, ids, w, exh, shh, tokens=tok)
-    assert_layer_close(out[tok], ref64, f"{cfg.name} sampled {len(tok)} tokens")
 
 
 # --------------------------------------------------------------------------- size limits

@@ -41,7 +41,12 @@
  *     ordered (same stream or synchronised).
  *   - Numbers: e4m3 is the OCP FP8 E4M3FN format (bias 7, max 448, no inf);
  *     bfloat16 is stored as its 16-bit pattern. Dequantised value = code *
- *     scale. Scales are float32.
+ *     scale. Scales are float32. Wherever values are quantised to e4m3 (x, and
+ *     the product h inside the grouped SwiGLU calls): a group's scale comes
+ *     from its largest non-NaN magnitude, a scaled value beyond +-448
+ *     saturates to +-448, and a NaN value (including inf / inf in a group
+ *     whose largest magnitude is infinite) gets a NaN code (0x7F or 0xFF; the
+ *     sign of a NaN code is unspecified).
  *   - No entry point uses floating-point atomics; results are bit-identical
  *     from run to run for the same inputs.
  */
@@ -131,7 +136,9 @@ moe_status moe_dispatch(const int32_t* topk_ids, int64_t N, int32_t K, int32_t E
  *   w_gate, w_up [E][d_ff][d] e4m3;  s_gate, s_up [E][d_ff/128][d/128] float32
  *   w_down [E][d][d_ff] e4m3;        s_down [E][d/128][d_ff/128] float32
  * y_sorted[N*K][d] bf16, in sorted-position order.
- * d and d_ff: positive multiples of 128, at most MOE_MAX_DIM. N = 0 is a no-op.
+ * d and d_ff: positive multiples of 128, at most MOE_MAX_DIM; N, K and E as
+ * moe_dispatch. N = 0 is a no-op. The workspace size queries return 0 for
+ * arguments the call would reject.
  * ---------------------------------------------------------------------- */
 size_t moe_swiglu_workspace_size(int64_t N, int32_t K, int32_t E, int32_t d, int32_t d_ff);
 
@@ -175,16 +182,19 @@ moe_status moe_grouped_swiglu_q(const uint8_t* xq, const float* xs, int64_t N, i
  * of token n as moe_grouped_swiglu computes it. The result equals
  * moe_grouped_swiglu followed by moe_combine (K = 1, no shared expert) bit for
  * bit, without the y_sorted round trip through memory.
- * x[N][d] bf16; offsets[E+1] and sorted_slot[N] from moe_dispatch with K = 1;
- * topk_w[N] float32; weights as moe_grouped_swiglu; out[N][d] bf16, which
- * must not overlap x. The workspace needs moe_swiglu_workspace_size(N, 1, E,
- * d, d_ff) bytes. A token whose id moe_dispatch left out (out of range, fast
- * mode) keeps its previous out row; every other row is written exactly once.
- * Shapes, alignment and flags as moe_grouped_swiglu. N = 0 is a no-op.
+ * x[N][d] bf16; offsets[E+1], sorted_slot[N] and slot_pos[N] from moe_dispatch
+ * with K = 1; topk_w[N] float32; weights as moe_grouped_swiglu; out[N][d]
+ * bf16, which must not overlap x. The workspace needs
+ * moe_swiglu_workspace_size(N, 1, E, d, d_ff) bytes. Every out row is written
+ * exactly once: a token whose id moe_dispatch left out (out of range, fast
+ * mode: slot_pos[n] outside [0, N)) gets a +0 row, as moe_combine gives a
+ * token with no valid choice. Shapes, alignment and flags as
+ * moe_grouped_swiglu. N = 0 is a no-op.
  * ---------------------------------------------------------------------- */
 moe_status moe_grouped_swiglu_top1(const uint16_t* x, int64_t N, int32_t E, int32_t d,
                                    int32_t d_ff, const int32_t* offsets,
-                                   const int32_t* sorted_slot, const float* topk_w,
+                                   const int32_t* sorted_slot, const int32_t* slot_pos,
+                                   const float* topk_w,
                                    const uint8_t* w_gate, const float* s_gate,
                                    const uint8_t* w_up, const float* s_up,
                                    const uint8_t* w_down, const float* s_down, uint16_t* out,
@@ -227,7 +237,7 @@ moe_status moe_combine_residual(const uint16_t* y_sorted, const int32_t* slot_po
  * code = e4m3(value / scale) with IEEE division, nearest-even, saturating.
  * This is the first step of moe_grouped_swiglu, exported on its own.
  * x[rows][cols] bf16 -> q[rows][cols] e4m3, s[rows][cols/128] float32.
- * cols: positive multiple of 128, at most MOE_MAX_DIM; rows >= 0.
+ * cols: positive multiple of 128, at most MOE_MAX_DIM; 0 <= rows < 2^31.
  * ---------------------------------------------------------------------- */
 moe_status moe_quantize_rows(const uint16_t* x, int64_t rows, int32_t cols, uint8_t* q, float* s,
                              void* stream);

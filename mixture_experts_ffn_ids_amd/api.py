@@ -198,7 +198,8 @@ def grouped_swiglu_top1(x: torch.Tensor, disp: Dispatch, topk_w: torch.Tensor, e
         raise ValueError("out must not overlap x")
     nb = lib().moe_swiglu_workspace_size(N, 1, E, d, d_ff)
     ws = _workspace(nb, x.device, "swiglu")
-    st = lib().moe_grouped_swiglu_top1(_p(x), N, E, d, d_ff, _p(disp.offsets), _p(disp.sorted_slot), _p(topk_w),
+    st = lib().moe_grouped_swiglu_top1(_p(x), N, E, d, d_ff, _p(disp.offsets), _p(disp.sorted_slot),
+                                       _p(disp.slot_pos), _p(topk_w),
                                        _p(ex.w_gate), _p(ex.s_gate), _p(ex.w_up), _p(ex.s_up), _p(ex.w_down),
                                        _p(ex.s_down), _p(out), _p(ws), ws.numel(), int(flags), _stream(x.device))
     check(st, "moe_grouped_swiglu_top1")

@@ -1,6 +1,7 @@
-// C ABI of libmoe: host-side validation, workspace layout, launches and the
-// per-kernel event profiler. The declarations and their contracts are in
-// include/moe.h.
+// C ABI of libmoe: host-side validation, workspace layout, tile-list sizing, launches
+// and the per-kernel event profiler. The declarations and their contracts are in
+// include/moe.h. This file holds no kernels: it also builds for the host alone, which
+// the sanitizer check of the host code uses.
 #include <math.h>
 #include <mutex>
 #include <string.h>
@@ -8,6 +9,29 @@
 
 #include "moe.h"
 #include "moe_internal.h"
+
+namespace moe {
+
+// ---------------------------------------------------------------- tile lists
+// BM (rows per tile) of each shape; the gate|up and down kernels of a shape share it
+// so that one tile list serves both.
+int tile_rows(TileShape shape) {
+    switch (shape) {
+        case TileShape::Rows16: return 16;
+        case TileShape::Rows128: return 128;
+        case TileShape::Rows192: return 192;
+        case TileShape::Rows224: return 224;
+        default: return 256;
+    }
+}
+
+int64_t max_tiles(int64_t rows, int E, int BM) {
+    // sum_e ceil(M_e / BM) <= rows / BM + (number of non-empty experts)
+    const int64_t nonempty = rows < E ? rows : E;
+    return rows / BM + nonempty + 1;
+}
+
+}  // namespace moe
 
 using namespace moe;
 
@@ -140,6 +164,11 @@ SwigluWs swiglu_layout(int64_t N, int32_t K, int32_t E, int32_t d, int32_t d_ff,
 
 bool dim_ok(int32_t v) { return v > 0 && v % kGroup == 0 && v <= MOE_MAX_DIM; }
 
+// 0 <= N, 1 <= K <= MOE_MAX_TOPK and N*K < 2^31, tested without forming an overflowing product
+bool slots_ok(int64_t N, int32_t K) {
+    return N >= 0 && K >= 1 && K <= MOE_MAX_TOPK && N <= 0x7fffffffLL / K;
+}
+
 // The many-row kernels address activations with 32-bit byte offsets from a per-block base:
 // token rows x d (gate|up) and sorted rows x d_ff (down) must stay below 2^32 bytes.
 // Larger batches use the 16-row kernel, which addresses with 64 bits.
@@ -192,16 +221,14 @@ const char* moe_status_string(int status) {
 int moe_last_hip_error(void) { return g_last_hip_error; }
 
 size_t moe_dispatch_workspace_size(int64_t N, int32_t K, int32_t E) {
-    if (N < 0 || K < 1 || E < 1) return 0;
+    if (!slots_ok(N, K) || E < 1 || E > MOE_MAX_EXPERTS || K > E) return 0;
     return dispatch_layout(N, K, E).total;
 }
 
 moe_status moe_dispatch(const int32_t* topk_ids, int64_t N, int32_t K, int32_t E, int32_t* counts,
                         int32_t* offsets, int32_t* sorted_slot, int32_t* slot_pos, void* workspace,
                         size_t workspace_bytes, uint32_t flags, void* stream) {
-    if (N < 0 || K < 1 || E < 1 || E > MOE_MAX_EXPERTS || K > MOE_MAX_TOPK || K > E ||
-        N * (int64_t)K > 0x7fffffffLL)
-        return MOE_ERR_SHAPE;
+    if (!slots_ok(N, K) || E < 1 || E > MOE_MAX_EXPERTS || K > E) return MOE_ERR_SHAPE;
     if (!counts || !offsets || !workspace) return MOE_ERR_NULL;
     if (N > 0 && (!topk_ids || !sorted_slot || !slot_pos)) return MOE_ERR_NULL;
     if (!aligned(topk_ids, 4) || !aligned(counts, 4) || !aligned(offsets, 4) || !aligned(sorted_slot, 4) ||
@@ -231,12 +258,12 @@ moe_status moe_dispatch(const int32_t* topk_ids, int64_t N, int32_t K, int32_t E
 }
 
 size_t moe_swiglu_workspace_size(int64_t N, int32_t K, int32_t E, int32_t d, int32_t d_ff) {
-    if (N < 0 || K < 1 || E < 1 || !dim_ok(d) || !dim_ok(d_ff)) return 0;
+    if (!slots_ok(N, K) || E < 1 || E > MOE_MAX_EXPERTS || K > E || !dim_ok(d) || !dim_ok(d_ff)) return 0;
     return swiglu_layout(N, K, E, d, d_ff).total;
 }
 
 size_t moe_swiglu_q_workspace_size(int64_t N, int32_t K, int32_t E, int32_t d, int32_t d_ff) {
-    if (N < 0 || K < 1 || E < 1 || !dim_ok(d) || !dim_ok(d_ff)) return 0;
+    if (!slots_ok(N, K) || E < 1 || E > MOE_MAX_EXPERTS || K > E || !dim_ok(d) || !dim_ok(d_ff)) return 0;
     return swiglu_layout(N, K, E, d, d_ff, false).total;
 }
 
@@ -253,15 +280,14 @@ moe_status grouped_swiglu(bool with_x, const uint16_t* x, const uint8_t* xq_in, 
                           const uint8_t* w_gate, const float* s_gate, const uint8_t* w_up, const float* s_up,
                           const uint8_t* w_down, const float* s_down, uint16_t* y_sorted, void* workspace,
                           size_t workspace_bytes, uint32_t flags, void* stream, const float* top1_w = nullptr,
-                          bool top1 = false) {
-    if (N < 0 || K < 1 || E < 1 || E > MOE_MAX_EXPERTS || K > MOE_MAX_TOPK || K > E || !dim_ok(d) ||
-        !dim_ok(d_ff) || N * (int64_t)K > 0x7fffffffLL)
+                          const int32_t* top1_slot_pos = nullptr, bool top1 = false) {
+    if (!slots_ok(N, K) || E < 1 || E > MOE_MAX_EXPERTS || K > E || !dim_ok(d) || !dim_ok(d_ff))
         return MOE_ERR_SHAPE;
     if (N == 0) return MOE_OK;
     if ((with_x ? !x : (!xq_in || !xs_in)) || !offsets || !sorted_slot || !w_gate || !s_gate || !w_up || !s_up ||
-        !w_down || !s_down || !y_sorted || !workspace || (top1 && !top1_w))
+        !w_down || !s_down || !y_sorted || !workspace || (top1 && (!top1_w || !top1_slot_pos)))
         return MOE_ERR_NULL;
-    if (top1 && !aligned(top1_w, 4)) return MOE_ERR_ALIGN;
+    if (top1 && (!aligned(top1_w, 4) || !aligned(top1_slot_pos, 4))) return MOE_ERR_ALIGN;
     if ((with_x ? !aligned(x, 16) : (!aligned(xq_in, 16) || !aligned(xs_in, 4))) || !aligned(w_gate, 16) ||
         !aligned(w_up, 16) || !aligned(w_down, 16) || !aligned(y_sorted, 16) || !aligned(workspace, 16) ||
         !aligned(offsets, 4) || !aligned(sorted_slot, 4) || !aligned(s_gate, 4) || !aligned(s_up, 4) ||
@@ -286,10 +312,12 @@ moe_status grouped_swiglu(bool with_x, const uint16_t* x, const uint8_t* xq_in, 
     const int64_t cap = max_tiles(rows, E, BM);
 
     if (with_x) {
-        // the tile list is built by the last workgroup of the quantisation launch
+        // the tile list is built by the last workgroup of the quantisation launch; for a top-1
+        // call the same launch also writes the +0 rows of the tokens the dispatch left out
         const TileJob job{offsets, E, rows, BM, cap, tiles, ntiles};
+        const ZeroRowsJob zero{top1_slot_pos, rows, y_sorted};
         ProfScope ps(MOE_KERNEL_QUANT, s);
-        MOE_HIP(launch_quantize_rows(x, N, d, ws + L.xq, (float*)(ws + L.xs), s, &job));
+        MOE_HIP(launch_quantize_rows(x, N, d, ws + L.xq, (float*)(ws + L.xs), s, &job, top1 ? &zero : nullptr));
     } else {
         ProfScope ps(MOE_KERNEL_DISPATCH, s);
         MOE_HIP(launch_build_tiles(offsets, E, rows, BM, cap, tiles, ntiles, s));
@@ -318,7 +346,7 @@ moe_status grouped_swiglu(bool with_x, const uint16_t* x, const uint8_t* xq_in, 
 moe_status combine(const uint16_t* y_sorted, const int32_t* slot_pos, const float* topk_w, const uint16_t* shared,
                    const uint16_t* residual, bool need_residual, int64_t N, int32_t K, int32_t d, uint16_t* out,
                    void* stream) {
-    if (N < 0 || K < 1 || K > MOE_MAX_TOPK || !dim_ok(d) || N * (int64_t)K > 0x7fffffffLL) return MOE_ERR_SHAPE;
+    if (!slots_ok(N, K) || !dim_ok(d)) return MOE_ERR_SHAPE;
     if (N == 0) return MOE_OK;
     if (!y_sorted || !slot_pos || !topk_w || !out || (need_residual && !residual)) return MOE_ERR_NULL;
     if (!aligned(y_sorted, 16) || !aligned(out, 16) || (shared && !aligned(shared, 16)) ||
@@ -346,12 +374,14 @@ moe_status moe_grouped_swiglu(const uint16_t* x, int64_t N, int32_t K, int32_t E
 }
 
 moe_status moe_grouped_swiglu_top1(const uint16_t* x, int64_t N, int32_t E, int32_t d, int32_t d_ff,
-                                   const int32_t* offsets, const int32_t* sorted_slot, const float* topk_w,
-                                   const uint8_t* w_gate, const float* s_gate, const uint8_t* w_up,
-                                   const float* s_up, const uint8_t* w_down, const float* s_down, uint16_t* out,
-                                   void* workspace, size_t workspace_bytes, uint32_t flags, void* stream) {
+                                   const int32_t* offsets, const int32_t* sorted_slot, const int32_t* slot_pos,
+                                   const float* topk_w, const uint8_t* w_gate, const float* s_gate,
+                                   const uint8_t* w_up, const float* s_up, const uint8_t* w_down,
+                                   const float* s_down, uint16_t* out, void* workspace, size_t workspace_bytes,
+                                   uint32_t flags, void* stream) {
     return grouped_swiglu(true, x, nullptr, nullptr, N, 1, E, d, d_ff, offsets, sorted_slot, w_gate, s_gate, w_up,
-                          s_up, w_down, s_down, out, workspace, workspace_bytes, flags, stream, topk_w, true);
+                          s_up, w_down, s_down, out, workspace, workspace_bytes, flags, stream, topk_w, slot_pos,
+                          true);
 }
 
 moe_status moe_grouped_swiglu_q(const uint8_t* xq, const float* xs, int64_t N, int32_t K, int32_t E, int32_t d,
@@ -377,7 +407,7 @@ moe_status moe_combine_residual(const uint16_t* y_sorted, const int32_t* slot_po
 
 moe_status moe_quantize_rows(const uint16_t* x, int64_t rows, int32_t cols, uint8_t* q, float* s_out,
                              void* stream) {
-    if (rows < 0 || !dim_ok(cols)) return MOE_ERR_SHAPE;
+    if (rows < 0 || rows > 0x7fffffffLL || !dim_ok(cols)) return MOE_ERR_SHAPE;
     if (rows == 0) return MOE_OK;
     if (!x || !q || !s_out) return MOE_ERR_NULL;
     if (!aligned(x, 16) || !aligned(q, 16) || !aligned(s_out, 4)) return MOE_ERR_ALIGN;

@@ -226,12 +226,6 @@ hipError_t launch_dispatch(const int32_t* ids, int64_t N, int K, int E, int32_t*
 }
 
 // ---------------------------------------------------------------- tile lists
-int64_t max_tiles(int64_t rows, int E, int BM) {
-    // sum_e ceil(M_e / BM) <= rows / BM + (number of non-empty experts)
-    const int64_t nonempty = rows < E ? rows : E;
-    return rows / BM + nonempty + 1;
-}
-
 __global__ __launch_bounds__(1024) void k_tiles(const int32_t* __restrict__ offsets, int E, int64_t rows,
                                                 int BM, int64_t cap, Tile* __restrict__ tiles,
                                                 int32_t* __restrict__ num_tiles) {

@@ -162,19 +162,28 @@ __global__ __launch_bounds__(WM* WN * 64) void k_grouped_gemm(const GemmParams P
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) acc[ten][mt][nt] = v4f{0.f, 0.f, 0.f, 0.f};
 
+    // gate|up sums each block exactly (bf16 matrix ops on widened codes: its results are
+    // requantised); down keeps the FP8 op (see mfma_block_exact)
     auto compute = [&](const Ops& o) {
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
+        for (int mt = 0; mt < MT; ++mt) {
+            Frag16 a16;
+            if constexpr (MODE == 0) a16 = widen(o.a[mt]);
 #pragma unroll
             for (int ten = 0; ten < NTEN; ++ten) {
                 const float f = o.as[mt] * o.sw[ten];
 #pragma unroll
                 for (int nt = 0; nt < NT; ++nt) {
-                    const v4f r = mfma_16x16x128_fp8(o.b[ten][nt], o.a[mt]);
+                    v4f r;
+                    if constexpr (MODE == 0)
+                        r = mfma_block_exact(widen(o.b[ten][nt]), a16);
+                    else
+                        r = mfma_16x16x128_fp8(o.b[ten][nt], o.a[mt]);
 #pragma unroll
                     for (int i = 0; i < 4; ++i) acc[ten][mt][nt][i] += f * r[i];
                 }
             }
+        }
     };
 
     // two register sets in turn: while one block is multiplied, the next is loading. The loads
@@ -267,19 +276,6 @@ __global__ __launch_bounds__(WM* WN * 64) void k_grouped_gemm(const GemmParams P
                 }
             }
         }
-    }
-}
-
-// ---------------------------------------------------------------- tile shapes
-// BM (rows per tile) of each shape; the gate|up and down kernels of a shape share it
-// so that one tile list serves both.
-int tile_rows(TileShape shape) {
-    switch (shape) {
-        case TileShape::Rows16: return 16;
-        case TileShape::Rows128: return 128;
-        case TileShape::Rows192: return 192;
-        case TileShape::Rows224: return 224;
-        default: return 256;
     }
 }
 

@@ -345,6 +345,18 @@ __global__ __launch_bounds__(512) void k_gemm_lds(const LdsGemmParams P) {
             v8i bf[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j) bf[j] = lds_frag(B, bbase[j] + rlane, kg);
+            // gate|up: the weight fragments widened once per block for the exact block sums
+            Frag16 bw[MODE == 0 ? 4 : 1];
+            if constexpr (MODE == 0) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) bw[j] = widen(bf[j]);
+            }
+            auto block_product = [&](int j, const v8i& a8, const Frag16& a16) -> v4f {
+                if constexpr (MODE == 0)
+                    return mfma_block_exact(bw[j], a16);
+                else
+                    return mfma_16x16x128_fp8(bf[j], a8);
+            };
             float sa[MT];
             if constexpr (MT % 2 == 0) {   // pairs are 8-byte aligned when MT is even
 #pragma unroll
@@ -392,16 +404,20 @@ __global__ __launch_bounds__(512) void k_gemm_lds(const LdsGemmParams P) {
                 const float f0 = sa[mt] * w0;
                 const float f1 = MODE == 0 ? sa[mt] * w1 : f0;
                 v4f r[4];
+                Frag16 a16;
+                if constexpr (MODE == 0) {
+                    if (FULL || mt < live_mt) a16 = widen(af);
+                }
                 if constexpr (DEFER) {
                     if (FULL || mt < live_mt) {
 #pragma unroll
-                        for (int j = 0; j < 4; ++j) r[j] = mfma_16x16x128_fp8(bf[j], af);
+                        for (int j = 0; j < 4; ++j) r[j] = block_product(j, af, a16);
                     }
                     if (mt > 0 && (FULL || mt - 1 < live_mt)) scale_add(mt - 1, rp, fp0, fp1);
                 } else if (FULL || mt < live_mt) {
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
-                        const v4f p = mfma_16x16x128_fp8(bf[j], af);
+                        const v4f p = block_product(j, af, a16);
                         const float f = (MODE == 0 && j >= 2) ? f1 : f0;
                         acc[mt][j][0] += f * p[0];
                         acc[mt][j][1] += f * p[1];

@@ -23,12 +23,17 @@ __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
     return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)f);
 }
 
-// Two floats -> two OCP e4m3 codes (nearest-even) in the low 16 bits; inputs are
-// clamped to +-448 first so that out-of-range values saturate.
+// Saturation to the largest finite e4m3 magnitude: |v| > 448 (infinities included) becomes
+// +-448. A NaN fails the comparison and passes through unchanged, so it is encoded as a NaN
+// code (the format has no infinity, and NaN is its only non-finite value).
+__device__ __forceinline__ float sat_e4m3(float v) {
+    return __builtin_fabsf(v) > kE4m3Max ? __builtin_copysignf(kE4m3Max, v) : v;
+}
+
+// Two floats -> two OCP e4m3 codes (nearest-even) in the low 16 bits; out-of-range values
+// saturate to +-448 first, NaNs give a NaN code (exponent and mantissa bits all ones).
 __device__ __forceinline__ uint32_t f32x2_to_e4m3(float a, float b) {
-    a = __builtin_fminf(__builtin_fmaxf(a, -kE4m3Max), kE4m3Max);
-    b = __builtin_fminf(__builtin_fmaxf(b, -kE4m3Max), kE4m3Max);
-    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false) & 0xffffu;
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(sat_e4m3(a), sat_e4m3(b), 0, false) & 0xffffu;
 }
 
 // silu(z) = z * sigmoid(z) with the hardware exponential and reciprocal (a few ulp; the
@@ -62,9 +67,54 @@ __device__ __forceinline__ void scale_group(float (&v)[NV], float s) {
 // 16x16x128 FP8 x FP8 -> FP32 matrix core op with unit block scales (E8M0 127 = 2^0).
 // Lane l supplies row (l & 15) of A and column (l & 15) of B, 32 K-values each;
 // the result holds D[4*(l>>4) + i][l & 15] in element i.
+// Its sum is not exact: measured on gfx950, the FP8 ops (this one and the 16x16x32 and
+// 32x32x64 forms alike) add their products in groups and align the group sums to the largest
+// one, dropping the bits below about 2^-14 of it (448*448 + 127*1 gives 200824, not 200831);
+// the error is up to ~7e-5 of the sum of |products|. Used where the result is not requantised
+// (the down projection), so that error stays far below the output tolerance.
 __device__ __forceinline__ v4f mfma_16x16x128_fp8(const v8i& a, const v8i& b) {
     const v4f zero = {0.f, 0.f, 0.f, 0.f};
     return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, zero, 0, 0, 0, 127, 0, 127);
+}
+
+// The same 128-wide block product with the sum formed exactly (to float32 rounding): every
+// e4m3 value is a bfloat16 value, so the fragment is widened to bfloat16 (one conversion per
+// two codes) and multiplied by four chained 16x16x32 bf16 ops, whose products and sums are
+// exact up to float32 roundings (measured: 448*448 + 127*1 gives 200831; error about 3e-8 of
+// the sum of |products|). Used for gate|up, whose results are requantised: an accumulation
+// error there moves e4m3 codes of h across rounding midpoints, and a moved code of a large h
+// element alone can exceed the output tolerance.
+// Widened fragment: k[j] holds the 8 values of bytes [8j, 8j+8) of the lane's 32 K-bytes, so
+// op j covers K-values 32 (l >> 4) + 8j + (0..7) for A and B alike, and the four ops together
+// the whole block.
+// The widening goes through float32 (v_cvt_pk_f32_fp8, then a round-to-nearest bf16 pack that
+// is exact here): measured on gfx950 over all 256 codes, that path reproduces every value. The
+// single-step v_cvt_scalef32_pk_bf16_fp8 (scale 1) did not: the second value of each pair
+// repeated the first.
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef float v2f __attribute__((ext_vector_type(2)));
+struct Frag16 {
+    v8bf k[4];
+};
+__device__ __forceinline__ v8bf widen8(uint32_t lo, uint32_t hi) {
+    const v2f p0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)lo, false);
+    const v2f p1 = __builtin_amdgcn_cvt_pk_f32_fp8((int)lo, true);
+    const v2f p2 = __builtin_amdgcn_cvt_pk_f32_fp8((int)hi, false);
+    const v2f p3 = __builtin_amdgcn_cvt_pk_f32_fp8((int)hi, true);
+    return v8bf{(__bf16)p0[0], (__bf16)p0[1], (__bf16)p1[0], (__bf16)p1[1],
+                (__bf16)p2[0], (__bf16)p2[1], (__bf16)p3[0], (__bf16)p3[1]};
+}
+__device__ __forceinline__ Frag16 widen(const v8i& f) {
+    Frag16 w;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) w.k[j] = widen8((uint32_t)f[2 * j], (uint32_t)f[2 * j + 1]);
+    return w;
+}
+__device__ __forceinline__ v4f mfma_block_exact(const Frag16& a, const Frag16& b) {
+    v4f c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.k[j], b.k[j], c, 0, 0, 0);
+    return c;
 }
 
 // ---------------------------------------------------------------- launchers
@@ -168,9 +218,18 @@ struct TileJob {
     const int32_t* offsets; int E; int64_t rows; int BM; int64_t cap; Tile* tiles; int32_t* num_tiles;
 };
 
-// Dynamic e4m3 quantisation of rows; with tile_job, the same launch also builds that tile list.
+// Rows of out[rows][cols] (bf16, the shape of the quantised x) to set to +0: those whose
+// slot_pos entry lies outside [0, slots), i.e. the tokens a top-1 dispatch left out, which
+// no GEMM epilogue writes. out == NULL: none.
+struct ZeroRowsJob {
+    const int32_t* slot_pos; int64_t slots; uint16_t* out;
+};
+
+// Dynamic e4m3 quantisation of rows; with tile_job, the same launch also builds that tile list;
+// with zero_job, it also zeroes those rows of zero_job->out.
 hipError_t launch_quantize_rows(const uint16_t* x, int64_t rows, int cols, uint8_t* q, float* s,
-                                hipStream_t stream, const TileJob* tile_job = nullptr);
+                                hipStream_t stream, const TileJob* tile_job = nullptr,
+                                const ZeroRowsJob* zero_job = nullptr);
 
 // num_tiles[2]: the number of tiles, and 1 if every expert with rows got exactly one tile
 hipError_t launch_build_tiles(const int32_t* offsets, int E, int64_t rows, int BM, int64_t max_tiles,

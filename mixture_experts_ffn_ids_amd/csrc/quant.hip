@@ -54,7 +54,8 @@ __device__ __forceinline__ void quant_group(const uint4 raw, uint2& codes, float
 // list instead (it does not depend on the quantised rows), which saves a launch.
 __global__ __launch_bounds__(256) void k_quantize_rows(const uint16_t* __restrict__ x, int64_t groups,
                                                        int cols, uint8_t* __restrict__ q,
-                                                       float* __restrict__ s, const TileJob job) {
+                                                       float* __restrict__ s, const TileJob job,
+                                                       const ZeroRowsJob zj) {
     const int qblocks = gridDim.x - (job.tiles ? 1 : 0);
     if ((int)blockIdx.x == qblocks) {   // only with a tile job
         build_tiles_block(job.offsets, job.E, job.rows, job.BM, job.cap, job.tiles, job.num_tiles);
@@ -88,6 +89,11 @@ __global__ __launch_bounds__(256) void k_quantize_rows(const uint16_t* __restric
             if (valid[h]) {
                 *reinterpret_cast<uint2*>(q + off[h]) = codes;
                 if (sub == 0) s[(g0 + h)] = sc;
+                if (zj.out) {   // a token left out by the dispatch: its output row is +0
+                    const int32_t p = zj.slot_pos[(g0 + h) / gpr];
+                    if (p < 0 || p >= zj.slots)
+                        *reinterpret_cast<uint4*>(zj.out + off[h]) = make_uint4(0, 0, 0, 0);
+                }
             }
         }
     }
@@ -201,9 +207,10 @@ hipError_t launch_rmsnorm_quantize(const uint16_t* x, const uint16_t* gain, floa
 }
 
 hipError_t launch_quantize_rows(const uint16_t* x, int64_t rows, int cols, uint8_t* q, float* s,
-                                hipStream_t stream, const TileJob* tile_job) {
+                                hipStream_t stream, const TileJob* tile_job, const ZeroRowsJob* zero_job) {
     const int64_t groups = rows * (cols / kGroup);
     const TileJob job = tile_job ? *tile_job : TileJob{};
+    const ZeroRowsJob zj = zero_job ? *zero_job : ZeroRowsJob{};
     if (groups == 0) {
         if (job.tiles)
             hipLaunchKernelGGL(k_tiles_only, dim3(1), dim3(256), 0, stream, job);
@@ -213,7 +220,8 @@ hipError_t launch_quantize_rows(const uint16_t* x, int64_t rows, int cols, uint8
     int64_t blocks = (threads + 255) / 256;
     if (blocks > 65536) blocks = 65536;
     if (job.tiles) ++blocks;
-    hipLaunchKernelGGL(k_quantize_rows, dim3((unsigned)blocks), dim3(256), 0, stream, x, groups, cols, q, s, job);
+    hipLaunchKernelGGL(k_quantize_rows, dim3((unsigned)blocks), dim3(256), 0, stream, x, groups, cols, q, s, job,
+                       zj);
     return hipGetLastError();
 }
 

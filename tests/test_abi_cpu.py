@@ -142,18 +142,21 @@ def test_fused_neighbour_calls_validate_on_host():
     q_ws = L.moe_swiglu_q_workspace_size(4, 2, 8, 128, 128)
     assert 0 < q_ws < L.moe_swiglu_workspace_size(4, 2, 8, 128, 128)
     assert L.moe_grouped_swiglu_q(p, p, 4, 2, 8, 128, 128, p, p, *args, p, q_ws - 1, 0, NULL) == 4
-    # top-1 experts with the combine in the down epilogue: weights required and 4-B aligned,
+    # top-1 experts with the combine in the down epilogue: slot_pos and weights required and 4-B aligned,
     # shapes and workspace checked like moe_grouped_swiglu (the workspace of K = 1)
     wargs = [p] * 6
-    assert L.moe_grouped_swiglu_top1(p, 4, 8, 128, 128, p, p, NULL, *wargs, p, p, 1 << 16, 0, NULL) == 1
-    assert L.moe_grouped_swiglu_top1(p, 4, 8, 128, 128, p, p, ctypes.c_void_p(p.value + 2), *wargs, p, p,
+    assert L.moe_grouped_swiglu_top1(p, 4, 8, 128, 128, p, p, p, NULL, *wargs, p, p, 1 << 16, 0, NULL) == 1
+    assert L.moe_grouped_swiglu_top1(p, 4, 8, 128, 128, p, p, NULL, p, *wargs, p, p, 1 << 16, 0, NULL) == 1
+    assert L.moe_grouped_swiglu_top1(p, 4, 8, 128, 128, p, p, p, ctypes.c_void_p(p.value + 2), *wargs, p, p,
                                      1 << 16, 0, NULL) == 3
-    assert L.moe_grouped_swiglu_top1(p, 4, 8, 130, 128, p, p, p, *wargs, p, p, 1 << 16, 0, NULL) == 2
-    assert L.moe_grouped_swiglu_top1(p, -1, 8, 128, 128, p, p, p, *wargs, p, p, 1 << 16, 0, NULL) == 2
+    assert L.moe_grouped_swiglu_top1(p, 4, 8, 128, 128, p, p, ctypes.c_void_p(p.value + 2), p, *wargs, p, p,
+                                     1 << 16, 0, NULL) == 3
+    assert L.moe_grouped_swiglu_top1(p, 4, 8, 130, 128, p, p, p, p, *wargs, p, p, 1 << 16, 0, NULL) == 2
+    assert L.moe_grouped_swiglu_top1(p, -1, 8, 128, 128, p, p, p, p, *wargs, p, p, 1 << 16, 0, NULL) == 2
     t1_ws = L.moe_swiglu_workspace_size(4, 1, 8, 128, 128)
-    assert L.moe_grouped_swiglu_top1(p, 4, 8, 128, 128, p, p, p, *wargs, p, p, t1_ws - 1, 0, NULL) == 4
-    assert L.moe_grouped_swiglu_top1(NULL, 0, 8, 128, 128, NULL, NULL, NULL, *([NULL] * 6), NULL, NULL, 0, 0,
-                                     NULL) == 0
+    assert L.moe_grouped_swiglu_top1(p, 4, 8, 128, 128, p, p, p, p, *wargs, p, p, t1_ws - 1, 0, NULL) == 4
+    assert L.moe_grouped_swiglu_top1(NULL, 0, 8, 128, 128, NULL, NULL, NULL, NULL, *([NULL] * 6), NULL, NULL, 0,
+                                     0, NULL) == 0
     # combine with the residual: the residual is required
     assert L.moe_combine_residual(p, p, p, NULL, NULL, 4, 2, 128, p, NULL) == 1
     assert L.moe_combine_residual(p, p, p, NULL, p, 4, 2, 130, p, NULL) == 2

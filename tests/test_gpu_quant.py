@@ -86,10 +86,16 @@ def test_quantize_every_bf16_value_against_one_scale(amax_bits):
     assert np.array_equal(q.cpu().numpy(), q_ref)
 
 
+def _is_nan_code(c: np.ndarray) -> np.ndarray:
+    return (np.asarray(c, np.uint8) & 0x7F) == 0x7F
+
+
 def test_group_with_an_infinity_keeps_finite_codes():
     """A group whose largest magnitude is infinite gets an infinite scale and every finite value
-    the code of a signed zero, as the oracle's division gives (the infinite element's own code is
-    not compared: the format has no infinity). The other group of the row is unaffected."""
+    the code of a signed zero, as the oracle's division gives. The infinite element itself is
+    inf / inf, a NaN: both sides give it a NaN code (the format has no infinity; the sign of a
+    NaN code carries no value, so only NaN-ness is compared there). The other group of the row
+    is unaffected."""
     x = np.linspace(-3, 3, 256, dtype=np.float32).reshape(1, 256)
     x[0, 5] = np.inf
     bits = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
@@ -99,4 +105,37 @@ def test_group_with_an_infinity_keeps_finite_codes():
     q_ref, s_ref = oracle.quant_rows_bf16(bits)
     assert np.array_equal(s.cpu().numpy().view(np.uint32), s_ref.view(np.uint32))
     finite = np.isfinite(x)
-    assert np.array_equal(q.cpu().numpy()[finite], q_ref[finite])
+    got = q.cpu().numpy()
+    assert np.array_equal(got[finite], q_ref[finite])
+    assert _is_nan_code(q_ref[~finite]).all() and _is_nan_code(got[~finite]).all()
+
+
+def test_nan_inputs_give_nan_codes():
+    """NaNs of either sign, among finite values, in groups of several magnitudes: the group scale
+    comes from the finite values alone on both sides (a NaN is never the largest magnitude), the
+    finite values' codes match bit for bit, and every NaN is encoded as a NaN code, never as a
+    saturated +-448 or any other finite code."""
+    rng = np.random.default_rng(81)
+    x = (rng.standard_normal((6, 512)) * np.exp2(rng.integers(-10, 10, (6, 1)))).astype(np.float32)
+    x[0, 3] = np.nan
+    x[1, 130] = -np.nan
+    x[2, ::5] = np.nan                       # many NaNs in every group of the row
+    x[3, :128] = np.nan                      # a group of NaNs only: scale 1, all codes NaN
+    x[4, 300] = np.inf                       # an infinity beside a NaN in one group
+    x[4, 301] = np.nan
+    bits = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    bits[1, 130] |= 0x8000                   # a NaN with the sign bit set
+    say("quantize rows holding NaNs")
+    q, s = moe.quantize_rows(bf16_dev(bits))
+    torch.cuda.synchronize()
+    q_ref, s_ref = oracle.quant_rows_bf16(bits)
+    assert np.array_equal(s.cpu().numpy().view(np.uint32), s_ref.view(np.uint32))
+    got = q.cpu().numpy()
+    vals = oracle.bf16_to_f32(bits)
+    scale = np.repeat(s_ref, 128, axis=1)
+    nonfinite = ~np.isfinite(vals) | ~np.isfinite(scale)
+    assert np.array_equal(got[~nonfinite], q_ref[~nonfinite])
+    nan_in = np.isnan(vals) | (np.isinf(vals) & np.isinf(scale))
+    assert _is_nan_code(q_ref[nan_in]).all()
+    assert _is_nan_code(got[nan_in]).all(), "a NaN was encoded as a finite code"
+    assert np.array_equal(got[nonfinite & ~nan_in], q_ref[nonfinite & ~nan_in])

@@ -72,19 +72,40 @@ def test_top1_empty_and_dropped_tokens():
     empty = torch.empty((0, CFG.d), dtype=torch.bfloat16, device="cuda")
     d0 = moe.dispatch(torch.empty((0, 1), dtype=torch.int32, device="cuda"), CFG.E)
     assert tuple(moe.grouped_swiglu_top1(empty, d0, torch.empty((0, 1), device="cuda"), exd).shape) == (0, CFG.d)
-    # ids out of range (fast-mode dispatch leaves those tokens out): their out rows are left as
-    # they were, every other row matches the unfused result
+    # ids out of range (fast-mode dispatch leaves those tokens out): their out rows become +0,
+    # as the unfused combine gives a token with no valid choice; every row matches the unfused
+    # result bit for bit, whatever out held before
     bad = ids.copy()
     bad[[3, 250, 699]] = CFG.E + 1
+    bad[500] = -1
     x_d, w_d = bf16_dev(x), torch.from_numpy(w).cuda()
     disp = moe.dispatch(torch.from_numpy(bad).cuda(), CFG.E)
-    out = torch.full((CFG.N, CFG.d), 7.0, dtype=torch.bfloat16, device="cuda")
-    say("top1 dropped tokens")
-    moe.grouped_swiglu_top1(x_d, disp, w_d, exd, out=out)
     ref = bits_host(_unfused(x_d, disp, w_d, exd, 0))
+    for flags in (0, moe.FLAG_TILE_16, moe.FLAG_TILE_192):
+        out = torch.full((CFG.N, CFG.d), 7.0, dtype=torch.bfloat16, device="cuda")
+        say(f"top1 dropped tokens flags={flags}")
+        moe.grouped_swiglu_top1(x_d, disp, w_d, exd, flags, out=out)
+        torch.cuda.synchronize()
+        got = bits_host(out)
+        assert np.array_equal(got, ref)
+        assert np.all(got[[3, 250, 500, 699]] == 0)
+
+
+def test_moe_layer_top1_dropped_token_is_zero():
+    """moe_layer with K = 1 and an out-of-range id (fast mode) returns +0 for that token and the
+    unfused result everywhere, not whatever the fresh output buffer held."""
+    x, ids, w, exh = _case()
+    exd = experts_dev(exh)
+    bad = ids.copy()
+    bad[[0, 17]] = CFG.E + 3
+    x_d, w_d, ids_d = bf16_dev(x), torch.from_numpy(w).cuda(), torch.from_numpy(bad).cuda()
+    # fill the caching allocator's free blocks with non-zero bytes first, so that a row left
+    # unwritten would show
+    junk = torch.full((CFG.N * CFG.d * 4,), 0x7F, dtype=torch.uint8, device="cuda")
+    del junk
+    say("moe_layer K=1 with out-of-range ids")
+    out = bits_host(moe.moe_layer(x_d, ids_d, w_d, exd))
     torch.cuda.synchronize()
-    got = bits_host(out)
-    keep = np.ones(CFG.N, bool)
-    keep[[3, 250, 699]] = False
-    assert np.array_equal(got[keep], ref[keep])
-    assert np.all(got[~keep] == bits_host(torch.full((1,), 7.0, dtype=torch.bfloat16))[0])
+    ref = bits_host(_unfused(x_d, moe.dispatch(ids_d, CFG.E), w_d, exd, 0))
+    assert np.array_equal(out, ref)
+    assert np.all(out[[0, 17]] == 0)

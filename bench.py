@@ -18,6 +18,12 @@ quantised product it writes.
 The CPU baseline is the plain oracle (test infrastructure) on a bounded sample of
 the same batch, on this host's cores.
 
+The default run measures the 256-token decode batch (the headline: tokens/s, and the gate|up
+kernel against the HBM roofline) and then, in the same process and on the same resident expert
+weights, the 8192-token prefill batch, reported under the key "k2_prefill_8192" with its own
+step time, tokens/s, roofline record and the layer's fractions of the HBM and FP8 matrix peaks
+(the metric's other half). --secondary picks another workload or none.
+
 For the dense workload (the dense block's SwiGLU MLP) a step is that MLP over the batch, run
 through the same kernels as one expert that every token visits (dense_swiglu).
 
@@ -46,6 +52,10 @@ def parse():
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="k2_decode_256")
+    ap.add_argument("--secondary", default=None,
+                    help="a second workload measured in the same process and reported under its own key "
+                         "(default: k2_prefill_8192 when --config is k2_decode_256, the other half of the "
+                         "metric; 'none' to skip). It reuses the resident expert weights when they are the same")
     ap.add_argument("--cpu-tokens", type=int, default=None,
                     help="rows of x in the oracle's CPU-baseline sample (default: whole batch up to "
                          "2048 * 2048 / (top_k * d_ff))")
@@ -106,29 +116,15 @@ def copy_calibration(nbytes: int):
     print(json.dumps({"copy_bytes": nbytes, "launches": 5}), flush=True)
 
 
-def main():
-    args = parse()
-    if args.copy_bytes:
-        copy_calibration(args.copy_bytes)
-        return
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this layer is built and measured on a single MI355X "
-              "(no sharding or collectives); run with --gpus 1", file=sys.stderr)
-        sys.exit(2)
-
+def measure(cfg, args, dev, graph: bool):
+    """Time `args.steps` steps of one workload after `args.warmup` warm-up steps. Returns the
+    result fields of that workload and the host inputs the CPU baseline needs."""
     import numpy as np
     import torch
 
     import mixture_experts_ffn_ids_amd as moe
-    from workloads import config_by_name, make_routing, make_x_bits
+    from workloads import make_routing, make_x_bits
     from workloads.gen import make_experts_device, make_shared_device
-
-    if not torch.cuda.is_available():
-        print("no GPU available", file=sys.stderr)
-        sys.exit(1)
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    cfg = config_by_name(args.config)
 
     # ---- inputs, resident in HBM before timing
     x_bits = make_x_bits(cfg)
@@ -188,7 +184,7 @@ def main():
                       [marks[i - 1].elapsed_time(marks[i]) for i in range(1, args.steps)])
 
     graph_result = None
-    if args.graph:
+    if graph:
         # the same step captured once in a HIP graph (the eager runs above sized the workspaces),
         # replayed W times untimed and K times timed
         side = torch.cuda.Stream()
@@ -262,7 +258,7 @@ def main():
                 "frac": round(achieved_gbs / HBM_PEAK_GBS, 4)}
     tokens_per_s = cfg.layer_tokens / (ms_per_step / 1e3)
     result = {
-        "metric": "MoE-layer tokens/s at K2 shapes",
+        "metric": "MoE-layer tokens/s at K2 shapes; % HBM roofline (decode), % FP8 MFMA (prefill)",
         "value": round(tokens_per_s, 2),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -310,38 +306,91 @@ def main():
                                      f"choices of a top-{cfg.shard_topk} router) over its {E} local experts, "
                                      f"sorted, run and put back in arrival order; tokens = rows / "
                                      f"{cfg.shard_topk}; the exchanges between GPUs are not part of the step")
-    # ---- CPU baseline: the oracle as it stands, on a bounded sample of the same batch
-    if not args.no_cpu_baseline:
-        import oracle
-        from workloads.gen import experts_to_host
-        # about 2048 evaluations of a 2048-wide expert per pass
-        n_cpu = args.cpu_tokens or max(1, min(N, 2048 * 2048 // (K * d_ff)))
-        tok = np.arange(n_cpu, dtype=np.int64)
-        exh = experts_to_host(experts, np.unique(ids[tok]))
-        shh = experts_to_host(shared) if shared is not None else None
-        threads = len(os.sched_getaffinity(0))
-        threads = min(threads, 16)
-        used = oracle.threads_used(threads)
-        # repeat the sample until about 10 s of CPU work has been timed (at most 32 passes)
-        passes = 0
-        t0 = time.perf_counter()
-        while True:
-            if args.block:
-                xn = oracle.rmsnorm_rows(h_bits[tok], g_bits, 1e-6)
-                oracle.moe_forward(xn, ids[tok], w[tok], exh, shh, threads=threads, residual=h_bits[tok])
-            else:
-                oracle.moe_forward(x_bits, ids, w, exh, shh, tokens=tok, threads=threads)
-            passes += 1
-            dt = time.perf_counter() - t0
-            if dt >= 10.0 or passes >= 32:
-                break
-        per_row = cfg.layer_tokens / N                # layer tokens per row of x
-        result["cpu_baseline"] = {"value": round(passes * n_cpu * per_row / dt, 3), "unit": "tokens/s",
-                                  "cores": used,
-                                  "kind": "oracle",
-                                  "sample": f"{passes} passes over the first {n_cpu} of the {N} rows of x in the "
-                                            f"same batch, {dt:.1f} s"}
+    ctx = {"x_bits": x_bits, "ids": ids, "w": w, "experts": experts, "shared": shared}
+    if args.block:
+        ctx.update(h_bits=h_bits, g_bits=g_bits)
     del out
+    return result, ctx
+
+
+def cpu_baseline(cfg, args, ctx) -> dict:
+    """The oracle as it stands, on a bounded sample of the same batch, on this host's cores."""
+    import numpy as np
+
+    import oracle
+    from workloads.gen import experts_to_host
+    x_bits, ids, w, experts, shared = (ctx[k] for k in ("x_bits", "ids", "w", "experts", "shared"))
+    N, K, d_ff = cfg.N, cfg.K, cfg.d_ff
+    # about 2048 evaluations of a 2048-wide expert per pass
+    n_cpu = args.cpu_tokens or max(1, min(N, 2048 * 2048 // (K * d_ff)))
+    tok = np.arange(n_cpu, dtype=np.int64)
+    exh = experts_to_host(experts, np.unique(ids[tok]))
+    shh = experts_to_host(shared) if shared is not None else None
+    # every core of the affinity mask, unless OMP_NUM_THREADS asks for fewer: a host that runs
+    # several GPUs' jobs gives each its share of the cores that way (16 per GPU on the MI355X
+    # hosts this was measured on)
+    threads = len(os.sched_getaffinity(0))
+    omp = os.environ.get("OMP_NUM_THREADS", "")
+    if omp.isdigit() and 0 < int(omp) < threads:
+        threads = int(omp)
+    used = oracle.threads_used(threads)
+    # repeat the sample until about 10 s of CPU work has been timed (at most 32 passes)
+    passes = 0
+    t0 = time.perf_counter()
+    while True:
+        if args.block:
+            xn = oracle.rmsnorm_rows(ctx["h_bits"][tok], ctx["g_bits"], 1e-6)
+            oracle.moe_forward(xn, ids[tok], w[tok], exh, shh, threads=threads, residual=ctx["h_bits"][tok])
+        else:
+            oracle.moe_forward(x_bits, ids, w, exh, shh, tokens=tok, threads=threads)
+        passes += 1
+        dt = time.perf_counter() - t0
+        if dt >= 10.0 or passes >= 32:
+            break
+    per_row = cfg.layer_tokens / N                # layer tokens per row of x
+    return {"value": round(passes * n_cpu * per_row / dt, 3), "unit": "tokens/s", "cores": used,
+            "kind": "oracle",
+            "sample": f"{passes} passes over the first {n_cpu} of the {N} rows of x in the same batch, {dt:.1f} s"}
+
+
+# fields of a secondary workload's record
+_SECONDARY_KEYS = ("value", "unit", "ms_per_step", "step_ms", "config", "roofline", "layer", "kernels")
+
+
+def main():
+    args = parse()
+    if args.copy_bytes:
+        copy_calibration(args.copy_bytes)
+        return
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this layer is built and measured on a single MI355X "
+              "(no sharding or collectives); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from workloads import config_by_name
+
+    if not torch.cuda.is_available():
+        print("no GPU available", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    cfg = config_by_name(args.config)
+    result, ctx = measure(cfg, args, dev, args.graph)
+    print(f"[bench] {cfg.name}: {result['ms_per_step']} ms/step", file=sys.stderr, flush=True)
+
+    secondary = args.secondary or ("k2_prefill_8192" if cfg.name == "k2_decode_256" else "none")
+    if secondary != "none":
+        scfg = config_by_name(secondary)
+        sres, _ = measure(scfg, args, dev, False)
+        result[scfg.name] = {k: sres[k] for k in _SECONDARY_KEYS}
+        result[scfg.name]["measured"] = ("in the same process after the headline workload, with the same "
+                                         "warm-up and step counts and the same timing")
+        print(f"[bench] {scfg.name}: {sres['ms_per_step']} ms/step", file=sys.stderr, flush=True)
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(cfg, args, ctx)
     print(json.dumps(result), flush=True)
 
 

@@ -150,6 +150,32 @@ moe_status moe_grouped_swiglu(const uint16_t* x, int64_t N, int32_t K, int32_t E
                               uint32_t flags, void* stream);
 
 /* ------------------------------------------------------------------------
+ * moe_grouped_swiglu for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same call and the same result, bit for bit, with no
+ * workspace argument. Its scratch (the quantised activations and product and
+ * the tile list) lives in a fixed array inside the library, one per GPU,
+ * MOE_NOALLOC_SCRATCH_BYTES long, held from the library's first use on a GPU
+ * until the process ends. The call allocates nothing. A problem whose
+ * moe_swiglu_workspace_size(N, K, E, d, d_ff) exceeds that size returns
+ * MOE_ERR_WORKSPACE with nothing enqueued (at Kimi-K2 shapes, d = 7168,
+ * d_ff = 2048, K = 8: up to about 2,600 tokens). Every call on a GPU uses that
+ * GPU's one array: calls that may overlap in time on one GPU (different
+ * streams without ordering between them) race on it and must not be made.
+ * Nothing in the array needs clearing between calls: each call writes what it
+ * reads. Other arguments, limits and errors as moe_grouped_swiglu.
+ * ---------------------------------------------------------------------- */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+moe_status moe_grouped_swiglu_noalloc(const uint16_t* x, int64_t N, int32_t K, int32_t E,
+                                      int32_t d, int32_t d_ff, const int32_t* offsets,
+                                      const int32_t* sorted_slot, const uint8_t* w_gate,
+                                      const float* s_gate, const uint8_t* w_up,
+                                      const float* s_up, const uint8_t* w_down,
+                                      const float* s_down, uint16_t* y_sorted, uint32_t flags,
+                                      void* stream);
+
+/* ------------------------------------------------------------------------
  * Grouped SwiGLU experts on activations already quantised: moe_grouped_swiglu
  * from its second step on, with xq/xs in place of the e4m3 quantisation of x.
  * For callers that produce the codes elsewhere: moe_rmsnorm_quantize_rows,

@@ -72,6 +72,8 @@ def _lib_handle():
         lib.moe_grouped_swiglu_top1.restype = st
         lib.moe_grouped_swiglu_top1.argtypes = [P, i64, i32, i32, i32, P, P, P, P, P, P, P, P, P, P, P, P, sz, u32,
                                                 P]
+        lib.moe_grouped_swiglu_noalloc.restype = st
+        lib.moe_grouped_swiglu_noalloc.argtypes = [P, i64, i32, i32, i32, i32, P, P, P, P, P, P, P, P, P, u32, P]
         lib.moe_rmsnorm_quantize_rows.restype = st
         lib.moe_rmsnorm_quantize_rows.argtypes = [P, P, ctypes.c_float, i64, i32, P, P, P, P]
         lib.moe_quantize_rows.restype = st

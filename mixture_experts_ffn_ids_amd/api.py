@@ -160,6 +160,24 @@ def grouped_swiglu(x: torch.Tensor, disp: Dispatch, experts, flags: int = 0,
     return out
 
 
+def grouped_swiglu_noalloc(x: torch.Tensor, disp: Dispatch, experts, flags: int = 0,
+                           out: torch.Tensor | None = None) -> torch.Tensor:
+    """grouped_swiglu without a workspace: the library's fixed per-GPU scratch array holds the
+    intermediates, so the call allocates nothing (out, when given, is the only output). Calls
+    that may overlap in time on one GPU must not be made; problems whose workspace would exceed
+    MOE_NOALLOC_SCRATCH_BYTES raise MOE_ERR_WORKSPACE."""
+    _want(x, torch.bfloat16, "x", 2)
+    N, d = x.shape
+    E, d_ff = _expert_dims(experts, d, N, disp)
+    ex, K = experts, disp.K
+    out = _y_out(out, N * K, d, x.device)
+    st = lib().moe_grouped_swiglu_noalloc(_p(x), N, K, E, d, d_ff, _p(disp.offsets), _p(disp.sorted_slot),
+                                          _p(ex.w_gate), _p(ex.s_gate), _p(ex.w_up), _p(ex.s_up), _p(ex.w_down),
+                                          _p(ex.s_down), _p(out), int(flags), _stream(x.device))
+    check(st, "moe_grouped_swiglu_noalloc")
+    return out
+
+
 def grouped_swiglu_q(xq: torch.Tensor, xs: torch.Tensor, disp: Dispatch, experts, flags: int = 0,
                      out: torch.Tensor | None = None, _ws_tag: str = "swiglu") -> torch.Tensor:
     """grouped_swiglu on activations already quantised: xq [N, d] uint8 e4m3 codes and

@@ -20,7 +20,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmoe.so")
-SOURCES = ["api.hip", "quant.hip", "dispatch.hip", "gemm.hip", "gemm_lds.hip", "combine.hip"]
+SOURCES = ["api.hip", "quant.hip", "dispatch.hip", "gemm.hip", "gemm_lds.hip", "combine.hip", "noalloc.hip"]
 ARCH = "gfx950"
 
 

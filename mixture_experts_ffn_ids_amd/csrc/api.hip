@@ -44,6 +44,12 @@ moe_status hip_fail(hipError_t e) {
     return MOE_ERR_HIP;
 }
 
+}  // namespace
+
+moe_status moe::record_hip_error(hipError_t e) { return hip_fail(e); }
+
+namespace {
+
 #define MOE_HIP(expr)                                 \
     do {                                              \
         hipError_t _e = (expr);                       \

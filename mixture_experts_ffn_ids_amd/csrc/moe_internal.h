@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "moe.h"
+
 namespace moe {
 
 constexpr int kGroup = 128;          // quantisation block edge (weight_block_size 128 x 128)
@@ -118,6 +120,9 @@ __device__ __forceinline__ v4f mfma_block_exact(const Frag16& a, const Frag16& b
 }
 
 // ---------------------------------------------------------------- launchers
+
+// Keeps e as the value moe_last_hip_error() reports on this thread; returns MOE_ERR_HIP.
+moe_status record_hip_error(hipError_t e);
 
 hipError_t launch_rmsnorm_quantize(const uint16_t* x, const uint16_t* gain, float eps, int64_t rows, int cols,
                                    uint16_t* y, uint8_t* q, float* s, hipStream_t stream);

@@ -197,12 +197,12 @@ TileShape choose_shape(int64_t N, int64_t rows, int32_t E, int32_t d, int32_t d_
     const int64_t per = touched > 0 ? rows / touched : 0;  // expected rows per touched expert
     if (per < 24) return TileShape::Rows16;
     if (per < 112) return TileShape::Rows128;
-    // a 224- or 256-row tile where one tile holds nearly every expert's rows (expert counts
-    // spread around their mean); experts with many more rows run faster in 192-row tiles,
-    // and 256-row tiles keep only a 2-stage weight ring
+    // a 224-row tile where one tile holds nearly every expert's rows (expert counts spread
+    // around their mean); experts with many more rows run faster in 192-row tiles. (The
+    // 256-row gate|up kernel, with its bf16 operands widened in registers, spills; it remains
+    // for the flag only.)
     if (per < 150 || per > 256) return TileShape::Rows192;
-    if (per < 200) return TileShape::Rows224;
-    return TileShape::Rows256;
+    return TileShape::Rows224;
 }
 
 }  // namespace

@@ -341,22 +341,58 @@ __global__ __launch_bounds__(512) void k_gemm_lds(const LdsGemmParams P) {
             const uint8_t* A = sA + (kb % NA) * C::A_BYTES;
             const uint8_t* B = sB + (kb % NBS) * C::B_BYTES;
             const float* SA = sSA + (kb % NA) * C::S_STAGE + sa_pos;
-            const float w0 = sSw0[kb], w1 = sSw1[kb];
             v8i bf[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j) bf[j] = lds_frag(B, bbase[j] + rlane, kg);
-            // gate|up: the weight fragments widened once per block for the exact block sums
-            Frag16 bw[MODE == 0 ? 4 : 1];
-            if constexpr (MODE == 0) {
+            // one row subtile at a time (a scheduling barrier after each keeps the compiler
+            // from gathering all of them, which would hold every fragment at once); the next
+            // subtile's activation fragment is read ahead.
+            auto scale_add = [&](int mt, const v4f (&r)[4], float f0, float f1) {
 #pragma unroll
-                for (int j = 0; j < 4; ++j) bw[j] = widen(bf[j]);
-            }
-            auto block_product = [&](int j, const v8i& a8, const Frag16& a16) -> v4f {
-                if constexpr (MODE == 0)
-                    return mfma_block_exact(bw[j], a16);
-                else
-                    return mfma_16x16x128_fp8(bf[j], a8);
+                for (int j = 0; j < 4; ++j) {
+                    const float f = (MODE == 0 && j >= 2) ? f1 : f0;
+                    acc[mt][j][0] += f * r[j][0];
+                    acc[mt][j][1] += f * r[j][1];
+                    acc[mt][j][2] += f * r[j][2];
+                    acc[mt][j][3] += f * r[j][3];
+                }
             };
+            v8i af = lds_frag(A, wm * MT * 16 + rlane, kg);
+            if constexpr (MODE == 0) {
+                // gate|up, exact block sums (mfma_block_exact4): the weight fragments are widened
+                // to bf16 once per block, each activation fragment just before its subtile's
+                // matrix ops. (Scaling the previous subtile's products and widening the next
+                // fragment while a subtile's ops run needs 32 more registers: it spills at 224
+                // rows and measured slower at 192.)
+                const float w0 = sSw0[kb], w1 = sSw1[kb];
+                Frag16 bw[4];
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) {
+                    v8i af_next;
+                    if (mt + 1 < MT) af_next = lds_frag(A, wm * MT * 16 + (mt + 1) * 16 + rlane, kg);
+                    if constexpr (ISSUE) {
+                        if (mt % (MT / SLOTS) == 0) {
+                            const int slot = mt / (MT / SLOTS);
+                            issue(next, slot * NQ / SLOTS, (slot + 1) * NQ / SLOTS);
+                        }
+                    }
+                    if (FULL || mt < live_mt) {
+                        if (mt == 0) {
+#pragma unroll
+                            for (int j = 0; j < 4; ++j) bw[j] = widen(bf[j]);
+                        }
+                        v4f r[4];
+                        mfma_block_exact4(bw, widen(af), r);
+                        const float sam = SA[mt];   // this subtile's row scale, read when needed
+                        scale_add(mt, r, sam * w0, sam * w1);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                    if (mt + 1 < MT) af = af_next;
+                }
+                return;
+            }
+            // down: one FP8 op per 128-wide block (its result is not requantised)
+            const float w0 = sSw0[kb];
             float sa[MT];
             if constexpr (MT % 2 == 0) {   // pairs are 8-byte aligned when MT is even
 #pragma unroll
@@ -369,28 +405,6 @@ __global__ __launch_bounds__(512) void k_gemm_lds(const LdsGemmParams P) {
 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt) sa[mt] = SA[mt];
             }
-            // one row subtile at a time (a scheduling barrier after each keeps the compiler
-            // from gathering all of them, which would hold every fragment at once); the next
-            // subtile's activation fragment is read ahead.
-            // DEFER (gate|up up to 192 rows): a subtile's products are scaled and accumulated
-            // after the next subtile's matrix ops are issued, so that the multiply-adds run
-            // while those execute instead of waiting for their own products (gate|up 3-4%
-            // faster on the shard and the dense MLP; with 224 and 256 rows, where it needs
-            // 240+ VGPRs, and in down it measured 1-4% slower).
-            constexpr bool DEFER = MODE == 0 && MT <= 6;
-            auto scale_add = [&](int mt, const v4f (&r)[4], float f0, float f1) {
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const float f = (MODE == 0 && j >= 2) ? f1 : f0;
-                    acc[mt][j][0] += f * r[j][0];
-                    acc[mt][j][1] += f * r[j][1];
-                    acc[mt][j][2] += f * r[j][2];
-                    acc[mt][j][3] += f * r[j][3];
-                }
-            };
-            v8i af = lds_frag(A, wm * MT * 16 + rlane, kg);
-            v4f rp[4];              // DEFER: raw products of the previous subtile
-            float fp0 = 0.0f, fp1 = 0.0f;
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
                 v8i af_next;
@@ -401,24 +415,11 @@ __global__ __launch_bounds__(512) void k_gemm_lds(const LdsGemmParams P) {
                         issue(next, slot * NQ / SLOTS, (slot + 1) * NQ / SLOTS);
                     }
                 }
-                const float f0 = sa[mt] * w0;
-                const float f1 = MODE == 0 ? sa[mt] * w1 : f0;
-                v4f r[4];
-                Frag16 a16;
-                if constexpr (MODE == 0) {
-                    if (FULL || mt < live_mt) a16 = widen(af);
-                }
-                if constexpr (DEFER) {
-                    if (FULL || mt < live_mt) {
-#pragma unroll
-                        for (int j = 0; j < 4; ++j) r[j] = block_product(j, af, a16);
-                    }
-                    if (mt > 0 && (FULL || mt - 1 < live_mt)) scale_add(mt - 1, rp, fp0, fp1);
-                } else if (FULL || mt < live_mt) {
+                if (FULL || mt < live_mt) {
+                    const float f = sa[mt] * w0;
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
-                        const v4f p = block_product(j, af, a16);
-                        const float f = (MODE == 0 && j >= 2) ? f1 : f0;
+                        const v4f p = mfma_16x16x128_fp8(bf[j], af);
                         acc[mt][j][0] += f * p[0];
                         acc[mt][j][1] += f * p[1];
                         acc[mt][j][2] += f * p[2];
@@ -426,16 +427,7 @@ __global__ __launch_bounds__(512) void k_gemm_lds(const LdsGemmParams P) {
                     }
                 }
                 __builtin_amdgcn_sched_barrier(0);
-                if constexpr (DEFER) {
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) rp[j] = r[j];
-                    fp0 = f0;
-                    fp1 = f1;
-                }
                 if (mt + 1 < MT) af = af_next;
-            }
-            if constexpr (DEFER) {
-                if (FULL || MT - 1 < live_mt) scale_add(MT - 1, rp, fp0, fp1);
             }
         };
 

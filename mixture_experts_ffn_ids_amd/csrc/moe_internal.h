@@ -2,6 +2,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <type_traits>
 #include <stdint.h>
 
 #include "moe.h"
@@ -89,22 +90,31 @@ __device__ __forceinline__ v4f mfma_16x16x128_fp8(const v8i& a, const v8i& b) {
 // Widened fragment: k[j] holds the 8 values of bytes [8j, 8j+8) of the lane's 32 K-bytes, so
 // op j covers K-values 32 (l >> 4) + 8j + (0..7) for A and B alike, and the four ops together
 // the whole block.
-// The widening goes through float32 (v_cvt_pk_f32_fp8, then a round-to-nearest bf16 pack that
-// is exact here): measured on gfx950 over all 256 codes, that path reproduces every value. The
-// single-step v_cvt_scalef32_pk_bf16_fp8 (scale 1) did not: the second value of each pair
-// repeated the first.
+// The widening is v_cvt_scalef32_pk_bf16_fp8 with a unit scale held in a register: op_sel 0
+// converts bytes 0 and 1 of the source, op_sel 1 bytes 2 and 3, one instruction per two codes.
+// Measured on gfx950 over all 256 codes, written this way it reproduces every value (and gives
+// NaN for the NaN codes). The compiler builtin of the same instruction, which encodes the scale
+// as an inline constant, was measured to repeat the first value of each pair instead.
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
-typedef float v2f __attribute__((ext_vector_type(2)));
 struct Frag16 {
     v8bf k[4];
 };
+__device__ __forceinline__ uint32_t widen2(uint32_t w, float one, std::false_type) {
+    uint32_t r;
+    asm("v_cvt_scalef32_pk_bf16_fp8 %0, %1, %2" : "=v"(r) : "v"(w), "v"(one));
+    return r;
+}
+__device__ __forceinline__ uint32_t widen2(uint32_t w, float one, std::true_type) {
+    uint32_t r;
+    asm("v_cvt_scalef32_pk_bf16_fp8 %0, %1, %2 op_sel:[1,0,0]" : "=v"(r) : "v"(w), "v"(one));
+    return r;
+}
 __device__ __forceinline__ v8bf widen8(uint32_t lo, uint32_t hi) {
-    const v2f p0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)lo, false);
-    const v2f p1 = __builtin_amdgcn_cvt_pk_f32_fp8((int)lo, true);
-    const v2f p2 = __builtin_amdgcn_cvt_pk_f32_fp8((int)hi, false);
-    const v2f p3 = __builtin_amdgcn_cvt_pk_f32_fp8((int)hi, true);
-    return v8bf{(__bf16)p0[0], (__bf16)p0[1], (__bf16)p1[0], (__bf16)p1[1],
-                (__bf16)p2[0], (__bf16)p2[1], (__bf16)p3[0], (__bf16)p3[1]};
+    const float one = 1.0f;
+    typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+    const v4u r = {widen2(lo, one, std::false_type{}), widen2(lo, one, std::true_type{}),
+                   widen2(hi, one, std::false_type{}), widen2(hi, one, std::true_type{})};
+    return __builtin_bit_cast(v8bf, r);
 }
 __device__ __forceinline__ Frag16 widen(const v8i& f) {
     Frag16 w;
@@ -117,6 +127,17 @@ __device__ __forceinline__ v4f mfma_block_exact(const Frag16& a, const Frag16& b
 #pragma unroll
     for (int j = 0; j < 4; ++j) c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.k[j], b.k[j], c, 0, 0, 0);
     return c;
+}
+// Four such block products sharing the second operand, r[n] = a[n] . b, with their chains
+// interleaved (quarter q of every product before quarter q + 1 of any), so that no matrix op
+// waits for the one just issued. Each r[n] is summed in the same order as mfma_block_exact.
+__device__ __forceinline__ void mfma_block_exact4(const Frag16 (&a)[4], const Frag16& b, v4f (&r)[4]) {
+#pragma unroll
+    for (int n = 0; n < 4; ++n) r[n] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int n = 0; n < 4; ++n) r[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[n].k[q], b.k[q], r[n], 0, 0, 0);
 }
 
 // ---------------------------------------------------------------- launchers

@@ -361,11 +361,14 @@ __global__ __launch_bounds__(512) void k_gemm_lds(const LdsGemmParams P) {
             if constexpr (MODE == 0) {
                 // gate|up, exact block sums (mfma_block_exact4): the weight fragments are widened
                 // to bf16 once per block, each activation fragment just before its subtile's
-                // matrix ops. (Scaling the previous subtile's products and widening the next
-                // fragment while a subtile's ops run needs 32 more registers: it spills at 224
-                // rows and measured slower at 192.)
+                // matrix ops.
+                // DEFER (up to 192 rows, where the 16 registers fit): a subtile's products are
+                // scaled into the accumulators after the next subtile's matrix ops are issued,
+                // so the wave does not wait for its own products.
+                constexpr bool DEFER = MT <= 6;
                 const float w0 = sSw0[kb], w1 = sSw1[kb];
                 Frag16 bw[4];
+                v4f rp[DEFER ? 4 : 1];
 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt) {
                     v8i af_next;
@@ -376,18 +379,36 @@ __global__ __launch_bounds__(512) void k_gemm_lds(const LdsGemmParams P) {
                             issue(next, slot * NQ / SLOTS, (slot + 1) * NQ / SLOTS);
                         }
                     }
+                    v4f r[4];
                     if (FULL || mt < live_mt) {
                         if (mt == 0) {
 #pragma unroll
                             for (int j = 0; j < 4; ++j) bw[j] = widen(bf[j]);
                         }
-                        v4f r[4];
                         mfma_block_exact4(bw, widen(af), r);
-                        const float sam = SA[mt];   // this subtile's row scale, read when needed
-                        scale_add(mt, r, sam * w0, sam * w1);
+                        if constexpr (!DEFER) {
+                            const float sam = SA[mt];   // this subtile's row scale, read when needed
+                            scale_add(mt, r, sam * w0, sam * w1);
+                        }
+                    }
+                    if constexpr (DEFER) {
+                        if (mt > 0 && (FULL || mt - 1 < live_mt)) {
+                            const float sam = SA[mt - 1];
+                            scale_add(mt - 1, rp, sam * w0, sam * w1);
+                        }
                     }
                     __builtin_amdgcn_sched_barrier(0);
+                    if constexpr (DEFER) {
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) rp[j] = r[j];
+                    }
                     if (mt + 1 < MT) af = af_next;
+                }
+                if constexpr (DEFER) {
+                    if (FULL || MT - 1 < live_mt) {
+                        const float sam = SA[MT - 1];
+                        scale_add(MT - 1, rp, sam * w0, sam * w1);
+                    }
                 }
                 return;
             }

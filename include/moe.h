@@ -125,10 +125,21 @@ moe_status moe_dispatch(const int32_t* topk_ids, int64_t N, int32_t K, int32_t E
  * with token n = sorted_slot[p] / K:
  *   xq = e4m3 quantisation of x[n], one scale per 128 features
  *        (scale = amax/448, code = e4m3(x/scale); an all-zero group has scale 1)
- *   g  = W_gate[e] xq,  u = W_up[e] xq         (d -> d_ff, float32 accumulation,
- *                                               per-128x128-block weight scales)
+ *   g  = W_gate[e] xq,  u = W_up[e] xq         (d -> d_ff, per-128x128-block weight scales)
  *   h  = silu(g) * u, requantised to e4m3 per 128 features (same rule)
  *   y_sorted[p] = bfloat16(W_down[e] h)        (d_ff -> d), unweighted.
+ * Accuracy delivered: each 128-wide block product of g and u (codes times codes)
+ * is summed exactly up to float32 rounding; each block product of the down
+ * projection is summed by the FP8 matrix op, which keeps about 14 bits below
+ * its largest partial sum (an error of up to about 7e-5 of the block's sum of
+ * |products|). Each block product is multiplied by its activation scale and
+ * weight block scale and added to a float32 accumulator, blocks in K order;
+ * silu uses the hardware exponential and reciprocal. A value of h close to an
+ * e4m3 rounding midpoint can therefore take the neighbouring code. Against the
+ * plain definition (exact dot products, exact silu), every token's output is
+ * within a relative L2 error of 1e-2 on the tested shapes, d = 7168 with
+ * d_ff = 2048 or 18432 and d_ff = 1024 with one choice per token among them
+ * (the largest seen: 8.7e-3, one choice per token, d_ff = 2048).
  *
  * x[N][d] bf16. offsets[E+1], sorted_slot[N*K] as produced by moe_dispatch
  * for the same N, K, E (other contents give unspecified but memory-safe

@@ -1,4 +1,5 @@
-// Grouped FP8 GEMMs of the routed experts on CDNA4 matrix cores.
+// Grouped GEMMs of the routed experts (e4m3 operands) on CDNA4 matrix cores, for tiles
+// of 16 rows (decode).
 //
 //   gate|up:  G, U [rows of expert e][d_ff] = Xq[rows] . W_gate[e]^T, . W_up[e]^T
 //             then h = silu(G) * U requantised to e4m3 per 128 features
@@ -12,8 +13,10 @@
 // One workgroup computes one (tile, n-block): a tile is up to BM consecutive
 // sorted rows of one expert (built on the device from the dispatch offsets), an
 // n-block is BN output columns (per weight tensor). The K loop walks 128-wide
-// blocks: one v_mfma_scale_f32_16x16x128_f8f6f4 covers exactly one quantisation
-// block, so each 16x16 partial product is scaled by (row scale x weight block
+// blocks, one quantisation block each. gate|up sums a block exactly: its e4m3
+// fragments are widened to bf16 in registers and multiplied by four 16x16x32 bf16
+// matrix ops (mfma_block_exact); down multiplies a block with one 16x16x128 FP8
+// matrix op. Each 16x16 block product is scaled by (row scale x weight block
 // scale) and added to the float32 accumulator -- the block-scale dequantisation
 // happens in the accumulator, never on the operands.
 //

@@ -1,13 +1,15 @@
-// Grouped FP8 GEMMs for tiles of many rows (prefill): both operands staged in LDS by
-// direct global->LDS copies, with a deeper ring for the weights than for the activations.
+// Grouped GEMMs (e4m3 operands) for tiles of many rows (prefill): both operands staged in
+// LDS by direct global->LDS copies, with a deeper ring for the weights than for the
+// activations.
 //
 // Same mathematics as gemm.hip ("SwiGLU output" page, evidence "mlp"; "Element-wise
 // product" page; FP8 block format from "Input features" page, evidence "linear"):
 //   gate|up: G, U = Xq[rows] . W_gate[e]^T, . W_up[e]^T -> h = silu(G) * U, e4m3 per 128
 //   down:    Y = Hq[rows] . W_down[e]^T -> bf16
-// One v_mfma_scale_f32_16x16x128_f8f6f4 per 128-wide quantisation block; each 16x16
-// partial is multiplied by (row activation scale x weight block scale) and added to the
-// fp32 accumulator.
+// Per 128-wide quantisation block: gate|up sums it exactly, its fragments widened to bf16
+// in registers and multiplied by four 16x16x32 bf16 matrix ops (mfma_block_exact4); down
+// uses one 16x16x128 FP8 matrix op. Each 16x16 block product is multiplied by (row
+// activation scale x weight block scale) and added to the fp32 accumulator.
 //
 // Workgroup: 8 waves (2 along the rows x 4 along the weight rows), 512 threads. It owns
 // one tile (<= BM = 32 MT sorted rows of one expert, MT = 4, 6, 7 or 8) and 256 weight rows:

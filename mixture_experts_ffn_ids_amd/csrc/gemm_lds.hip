@@ -283,9 +283,8 @@ __global__ __launch_bounds__(512) void k_gemm_lds(const LdsGemmParams P) {
         constexpr bool STREAM = decltype(stream)::value;
         constexpr int NQ = BW ? C::B_Q : C::A_Q + 1;  // copies per block (A: rows + scales)
         constexpr int NR = BW ? NBS : NA;             // ring depth
-        constexpr bool KEEP_OFF = true;               // offsets held in registers
         // byte offset of copy i in block 0: in the activations (A) or the weight tensor (B);
-        // the host keeps both below 2^32
+        // the host keeps both below 2^32. Computed once per item and held in registers.
         auto off = [&](int i) -> uint32_t {
             const int r = 8 * (rw + i * C::ROLE_W) + lrow;
             if constexpr (!BW) {
@@ -296,18 +295,13 @@ __global__ __launch_bounds__(512) void k_gemm_lds(const LdsGemmParams P) {
                 return (uint32_t)wrow * (uint32_t)P.Kdim + lchunk * 16;
             }
         };
-        uint32_t cIdx[KEEP_OFF ? NQ : 1];
+        uint32_t cIdx[NQ];
         auto plan = [&]() {
-            if constexpr (KEEP_OFF) {
 #pragma unroll
-                for (int i = 0; i < NQ; ++i) cIdx[i] = (!BW && i == C::A_Q) ? 0u : off(i);
-            }
+            for (int i = 0; i < NQ; ++i) cIdx[i] = (!BW && i == C::A_Q) ? 0u : off(i);
             if constexpr (!BW)
                 sOff = lane < C::S_L ? (uint32_t)sRow[scale_slot_row<MT>(rw * C::S_L + lane)] * (uint32_t)KB * 4u
                                      : 0u;
-        };
-        auto get_off = [&](int i) -> uint32_t {
-            if constexpr (KEEP_OFF) return cIdx[i]; else return off(i);
         };
         // issue copies [lo, hi) of block kb
         auto issue = [&](int kb, int lo, int hi) {
@@ -317,16 +311,16 @@ __global__ __launch_bounds__(512) void k_gemm_lds(const LdsGemmParams P) {
                 if (i < lo || i >= hi) continue;
                 if constexpr (!BW) {
                     if (i < C::A_Q)
-                        copy16(P.a + ko, get_off(i), ldsA + (kb % NA) * C::A_BYTES + i * C::ROLE_W * 1024);
+                        copy16(P.a + ko, cIdx[i], ldsA + (kb % NA) * C::A_BYTES + i * C::ROLE_W * 1024);
                     else
                         copy4(P.as + kb, sOff, ldsS + (kb % NA) * C::S_STAGE * 4);
                 } else {
                     const void* src = (MODE == 0 && i >= C::B_Q / 2 ? wBase1 : wBase0) + ko;
                     const uint32_t dst = ldsB + (kb % NBS) * C::B_BYTES + i * C::ROLE_W * 1024;
                     if constexpr (STREAM)
-                        copy16_nt(src, get_off(i), dst);
+                        copy16_nt(src, cIdx[i], dst);
                     else
-                        copy16(src, get_off(i), dst);
+                        copy16(src, cIdx[i], dst);
                 }
             }
         };

@@ -73,6 +73,7 @@ __global__ __launch_bounds__(256) void k_quantize_rows(const uint16_t* __restric
         uint4 raw[2];
         bool valid[2];
         int64_t off[2];
+        int32_t pos[2] = {0, 0};   // with the zero-rows job: the row's slot_pos entry
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const int64_t g = g0 + h;
@@ -80,6 +81,8 @@ __global__ __launch_bounds__(256) void k_quantize_rows(const uint16_t* __restric
             const int64_t row = valid[h] ? g / gpr : 0;
             off[h] = row * cols + (valid[h] ? (g % gpr) * kGroup + sub * 8 : 0);
             raw[h] = valid[h] ? *reinterpret_cast<const uint4*>(x + off[h]) : make_uint4(0, 0, 0, 0);
+            // loaded with the row, so that its latency overlaps the row's
+            if (zj.out && valid[h]) pos[h] = zj.slot_pos[row];
         }
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
@@ -90,8 +93,7 @@ __global__ __launch_bounds__(256) void k_quantize_rows(const uint16_t* __restric
                 *reinterpret_cast<uint2*>(q + off[h]) = codes;
                 if (sub == 0) s[(g0 + h)] = sc;
                 if (zj.out) {   // a token left out by the dispatch: its output row is +0
-                    const int32_t p = zj.slot_pos[(g0 + h) / gpr];
-                    if (p < 0 || p >= zj.slots)
+                    if (pos[h] < 0 || pos[h] >= zj.slots)
                         *reinterpret_cast<uint4*>(zj.out + off[h]) = make_uint4(0, 0, 0, 0);
                 }
             }

@@ -137,6 +137,36 @@ def test_zero_input_gives_zero_output():
 
 
 # --------------------------------------------------------------------------- size limits
+def test_non_finite_inputs_give_nan_tokens_only():
+    # x holds a NaN, a +inf and a -inf in three tokens. The quantiser's reading: an infinite
+    # amax makes the group's scale infinite, x/s is then NaN for the infinite element, and a
+    # NaN is encoded as the NaN code. So those tokens' outputs are NaN in every element, as
+    # the oracle's are; every other token is untouched and within the layer tolerance, and
+    # identical at every tile height.
+    cfg = Config("nonfinite", 40, 384, 256, 6, 2, "normal", "uniform", "dirichlet", False, seed=41)
+    x = make_x_bits(cfg).copy()
+    x[3, 5] = 0x7FC0     # NaN
+    x[7, 200] = 0x7F80   # +inf
+    x[11, 0] = 0xFF80    # -inf
+    ids, w = make_routing(cfg)
+    exh = make_experts_host(cfg)
+    _, ref64 = oracle.moe_forward(x, ids, w, exh)
+    bad = np.array([3, 7, 11])
+    good = np.setdiff1d(np.arange(cfg.N), bad)
+    assert np.isnan(ref64[bad]).all() and np.isfinite(ref64[good]).all()
+    exd = experts_dev(exh)
+    first = None
+    for shape in ("auto", "16", "128", "192", "224", "256"):
+        say(f"layer nonfinite shape={shape}")
+        out = _layer(x, ids, w, exd, None, 0 if shape == "auto" else SHAPES[shape])
+        assert np.isnan(oracle.bf16_to_f32(out[bad])).all(), f"nonfinite/{shape}: a poisoned token is not all NaN"
+        assert_layer_close(out[good], ref64[good], f"nonfinite/{shape}")
+        if first is None:
+            first = out[good]
+        else:
+            assert np.array_equal(out[good], first), f"nonfinite: {shape} differs on the finite tokens"
+
+
 def test_maximum_hidden_size():
     # d = 65536 = MOE_MAX_DIM: 512 K blocks per gate|up row, which exactly fills the many-row
     # kernels' table of weight block scales; every tile height, against the oracle

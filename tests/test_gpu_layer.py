@@ -103,6 +103,28 @@ def test_skew_multiple_row_tiles():
     _check_small(cfg, ids, w)
 
 
+@pytest.mark.parametrize("K", [1, 2])
+def test_expert_rows_at_tile_boundaries(K):
+    # experts holding exactly one tile of each height, and one row more (a last tile of one
+    # row): every tile edge of the 16-, 128-, 192- and 224-row kernels. K = 2: the gate|up
+    # gather and the combine see every edge; K = 1: the down epilogue's top-1 combine does.
+    counts = np.array([16, 17, 128, 129, 192, 193, 224, 225])
+    E = len(counts)
+    N = int(counts.sum()) // K
+    cfg = Config(f"tile_edges_k{K}", N, 256, 256, E, K, "normal", "uniform", "dirichlet", False, seed=51)
+    slots = np.repeat(np.arange(E, dtype=np.int32), counts)       # expert of each slot
+    rng = np.random.default_rng(52)
+    # token t takes slots t, t + N, ... of the slots sorted by expert: its experts differ,
+    # since no expert holds more than N slots
+    assert counts.max() <= N
+    ids = np.stack([slots[k * N:(k + 1) * N] for k in range(K)], axis=1)
+    assert K == 1 or np.all(ids[:, 0] != ids[:, 1])
+    ids = ids[rng.permutation(N)]
+    w = rng.dirichlet(np.ones(K), size=N).astype(np.float32)
+    assert np.array_equal(np.bincount(ids.reshape(-1), minlength=E), counts)
+    _check_small(cfg, ids, w)
+
+
 def test_many_choices_per_token():
     # K = 12 > 8: the combine's second batch of source rows, part-filled; d = 1536: the second
     # 1024-column slice of a token covers only half a wave; with the shared expert

@@ -170,7 +170,7 @@ moe_status moe_grouped_swiglu(const uint16_t* x, int64_t N, int32_t K, int32_t E
  * until the process ends. The call allocates nothing. A problem whose
  * moe_swiglu_workspace_size(N, K, E, d, d_ff) exceeds that size returns
  * MOE_ERR_WORKSPACE with nothing enqueued (at Kimi-K2 shapes, d = 7168,
- * d_ff = 2048, K = 8: up to about 2,600 tokens). Every call on a GPU uses that
+ * d_ff = 2048, K = 8, E = 384: up to 2,760 tokens). Every call on a GPU uses that
  * GPU's one array: calls that may overlap in time on one GPU (different
  * streams without ordering between them) race on it and must not be made.
  * Nothing in the array needs clearing between calls: each call writes what it

@@ -111,6 +111,20 @@ def test_workspace_sizes_scale_with_shapes():
     assert L.moe_swiglu_workspace_size(16, 8, 384, 7000, 2048) == 0
 
 
+def test_noalloc_scratch_limit_at_k2_shapes():
+    # the header's limit for moe_grouped_swiglu_noalloc at Kimi-K2 shapes: 2,760 tokens fit its
+    # 64 MiB scratch, 2,761 do not
+    hdr = open(os.path.join(ROOT, "include", "moe.h")).read()
+    m = re.search(r"#define MOE_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", hdr)
+    assert m, "MOE_NOALLOC_SCRATCH_BYTES not found"
+    cap = int(m.group(1)) << int(m.group(2))
+    assert cap == 64 << 20
+    assert "up to 2,760 tokens" in hdr
+    L = _lib.lib()
+    assert L.moe_swiglu_workspace_size(2760, 8, 384, 7168, 2048) <= cap
+    assert L.moe_swiglu_workspace_size(2761, 8, 384, 7168, 2048) > cap
+
+
 def test_profile_api_without_gpu():
     L = _lib.lib()
     ms = ctypes.c_double()

@@ -58,6 +58,75 @@ __device__ __forceinline__ v8i load_frag_global(const uint8_t* p) {
     return r;
 }
 
+// A weight fragment (16 weight rows x one 128-wide K block, in load_frag_global's layout)
+// read as whole cache lines. Each row's 128-byte block is one line. In the fragment layout a
+// lane holds 32 bytes of its own row, so a 16-byte load per lane can cover only half of each
+// of the 16 rows' lines, and with the nontemporal hint such half-line loads stream slowly.
+// Measured on this chip, streaming a weight matrix: half-line loads 6.0 TB/s, 5.0 with the
+// hint; whole-line loads 6.2-6.3, and 7.0-7.1 TB/s with the hint.
+// So the two loads cover rows 0-7 and rows 8-15 of the subtile, eight whole lines each
+// (`rows_lo`: lane l at row l & 7, 16-byte chunk l >> 3; `rows_hi`: the same 8 rows further),
+// and DPP moves hand each chunk to the lane that owns its row: lane l (row l & 15, K group
+// l >> 4) needs chunks 2 (l >> 4) and 2 (l >> 4) + 1 of its row, which are held by lane l
+// itself and by lane l ^ 8, i.e. 8 lanes along within its 16-lane row (row_ror:8).
+// The weights are read by one wave each, so the hint costs no reuse. The moves are made where
+// the fragment is used, so that the loads stay in flight until then.
+typedef int v4i __attribute__((ext_vector_type(4)));
+struct LineFrag {
+    v4i lo, hi;   // rows 0-7 and rows 8-15 of the subtile, as loaded
+};
+__device__ __forceinline__ LineFrag load_frag_lines(const uint8_t* rows_lo, const uint8_t* rows_hi) {
+    return {__builtin_nontemporal_load(reinterpret_cast<const v4i*>(rows_lo)),
+            __builtin_nontemporal_load(reinterpret_cast<const v4i*>(rows_hi))};
+}
+__device__ __forceinline__ v8i frag_from_lines(const LineFrag& f) {
+    constexpr int kRor8 = 0x128;   // DPP row_ror:8
+    v8i r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        // first 16 bytes: lanes 0-7 of each 16-lane row keep their own chunk of rows 0-7;
+        // lanes 8-15 take rows 8-15's chunk from lane l ^ 8 (banks 2 and 3 written)
+        r[i] = __builtin_amdgcn_update_dpp(f.lo[i], f.hi[i], kRor8, 0xF, 0xC, false);
+        // second 16 bytes: lanes 8-15 keep their own chunk of rows 8-15; lanes 0-7 take rows
+        // 0-7's chunk from lane l ^ 8 (banks 0 and 1 written)
+        r[4 + i] = __builtin_amdgcn_update_dpp(f.hi[i], f.lo[i], kRor8, 0xF, 0x3, false);
+    }
+    return r;
+}
+// The same for the exact-sum path: each loaded chunk is widened to bf16 first and the widened
+// dwords are moved. Widening a DPP result measured wrong on this chip (whole batches of NaN),
+// while widening loaded data is exact, as everywhere else in the library. The widening is
+// inline assembly, which the compiler's hazard check does not see as a vector ALU write, so
+// an s_nop after each conversion gives a DPP read of its result the two wait states it needs.
+__device__ __forceinline__ void widen_chunk(const v4i& c, uint32_t (&w)[8]) {
+    const float one = 1.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        asm("v_cvt_scalef32_pk_bf16_fp8 %0, %1, %2\n\ts_nop 1" : "=v"(w[2 * i]) : "v"(c[i]), "v"(one));
+        asm("v_cvt_scalef32_pk_bf16_fp8 %0, %1, %2 op_sel:[1,0,0]\n\ts_nop 1" : "=v"(w[2 * i + 1]) : "v"(c[i]), "v"(one));
+    }
+}
+__device__ __forceinline__ Frag16 widened_frag_from_lines(const LineFrag& f) {
+    constexpr int kRor8 = 0x128;   // DPP row_ror:8
+    uint32_t a[8], b[8], lo[8], hi[8];
+    widen_chunk(f.lo, a);
+    widen_chunk(f.hi, b);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        lo[i] = (uint32_t)__builtin_amdgcn_update_dpp((int)a[i], (int)b[i], kRor8, 0xF, 0xC, false);
+        hi[i] = (uint32_t)__builtin_amdgcn_update_dpp((int)b[i], (int)a[i], kRor8, 0xF, 0x3, false);
+    }
+    // Frag16 k[j] holds the widened dwords 2j, 2j+1 of the fragment: the first chunk gives
+    // k[0] and k[1], the second k[2] and k[3]
+    typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+    Frag16 r;
+    r.k[0] = __builtin_bit_cast(v8bf, (v4u){lo[0], lo[1], lo[2], lo[3]});
+    r.k[1] = __builtin_bit_cast(v8bf, (v4u){lo[4], lo[5], lo[6], lo[7]});
+    r.k[2] = __builtin_bit_cast(v8bf, (v4u){hi[0], hi[1], hi[2], hi[3]});
+    r.k[3] = __builtin_bit_cast(v8bf, (v4u){hi[4], hi[5], hi[6], hi[7]});
+    return r;
+}
+
 
 
 // MODE 0: gate|up with the silu*up requant epilogue; MODE 1: down with bf16 output.
@@ -124,15 +193,20 @@ __global__ __launch_bounds__(WM* WN * 64) void k_grouped_gemm(const GemmParams P
     const int cblk = (wave_live ? wcol0 : 0) / 128;   // its 128-row weight scale block
     const uint8_t* W[2] = {P.w0, P.w1};
     const float* S[2] = {P.s0, P.s1};
-    const uint8_t* bptr[NTEN][NT];
+    // weight fragments as whole lines (load_frag_lines): rows (lane & 7) and 8 + (lane & 7) of
+    // each 16-row subtile, 16-byte chunk (lane >> 3) of the K block
+    const uint8_t* bptr[NTEN][NT][2];
     const float* swptr[NTEN];
 #pragma unroll
     for (int ten = 0; ten < NTEN; ++ten) {
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
-            int col = wcol0 + nt * 16 + (lane & 15);
-            col = col < P.Ndim ? col : P.Ndim - 1;   // columns past the end are never stored
-            bptr[ten][nt] = W[ten] + ((int64_t)e * P.Ndim + col) * P.Kdim + kq;
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                int col = wcol0 + nt * 16 + 8 * h + (lane & 7);
+                col = col < P.Ndim ? col : P.Ndim - 1;   // columns past the end are never stored
+                bptr[ten][nt][h] = W[ten] + ((int64_t)e * P.Ndim + col) * P.Kdim + 16 * (lane >> 3);
+            }
         }
         swptr[ten] = S[ten] + ((int64_t)e * NB128 + cblk) * KB;
     }
@@ -140,7 +214,7 @@ __global__ __launch_bounds__(WM* WN * 64) void k_grouped_gemm(const GemmParams P
     struct Ops {
         v8i a[MT];
         float as[MT];
-        v8i b[NTEN][NT];
+        LineFrag b[NTEN][NT];
         float sw[NTEN];   // weight block scales (uniform: scalar loads)
     };
     auto load = [&](int kb, Ops& o) {
@@ -152,7 +226,8 @@ __global__ __launch_bounds__(WM* WN * 64) void k_grouped_gemm(const GemmParams P
 #pragma unroll
         for (int ten = 0; ten < NTEN; ++ten)
 #pragma unroll
-            for (int nt = 0; nt < NT; ++nt) o.b[ten][nt] = load_frag_global(bptr[ten][nt] + kb * 128);
+            for (int nt = 0; nt < NT; ++nt)
+                o.b[ten][nt] = load_frag_lines(bptr[ten][nt][0] + kb * 128, bptr[ten][nt][1] + kb * 128);
 #pragma unroll
         for (int ten = 0; ten < NTEN; ++ten) o.sw[ten] = swptr[ten][kb];
     };
@@ -179,9 +254,9 @@ __global__ __launch_bounds__(WM* WN * 64) void k_grouped_gemm(const GemmParams P
                 for (int nt = 0; nt < NT; ++nt) {
                     v4f r;
                     if constexpr (MODE == 0)
-                        r = mfma_block_exact(widen(o.b[ten][nt]), a16);
+                        r = mfma_block_exact(widened_frag_from_lines(o.b[ten][nt]), a16);
                     else
-                        r = mfma_16x16x128_fp8(o.b[ten][nt], o.a[mt]);
+                        r = mfma_16x16x128_fp8(frag_from_lines(o.b[ten][nt]), o.a[mt]);
 #pragma unroll
                     for (int i = 0; i < 4; ++i) acc[ten][mt][nt][i] += f * r[i];
                 }

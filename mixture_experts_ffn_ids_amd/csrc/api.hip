@@ -195,7 +195,11 @@ TileShape choose_shape(int64_t N, int64_t rows, int32_t E, int32_t d, int32_t d_
     }
     const int64_t touched = rows < E ? rows : E;
     const int64_t per = touched > 0 ? rows / touched : 0;  // expected rows per touched expert
-    if (per < 24) return TileShape::Rows16;
+    // The 16-row kernel streams weights fastest, but it reads an expert's weights once per
+    // 16-row tile, and above about 6 rows per expert the 128-row kernel, which reads them once,
+    // is faster (measured at K2 shapes: 2.62 vs 2.63 ms at 5.3 rows, 2.68 vs 2.64 at 6.7, 5.35
+    // vs 2.82 at 21).
+    if (per < 6) return TileShape::Rows16;
     if (per < 112) return TileShape::Rows128;
     // a 224-row tile where one tile holds nearly every expert's rows (expert counts spread
     // around their mean); experts with many more rows run faster in 192-row tiles. (The

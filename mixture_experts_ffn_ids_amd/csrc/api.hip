@@ -200,13 +200,22 @@ TileShape choose_shape(int64_t N, int64_t rows, int32_t E, int32_t d, int32_t d_
     // is faster (measured at K2 shapes: 2.62 vs 2.63 ms at 5.3 rows, 2.68 vs 2.64 at 6.7, 5.35
     // vs 2.82 at 21).
     if (per < 6) return TileShape::Rows16;
-    if (per < 112) return TileShape::Rows128;
-    // a 224-row tile where one tile holds nearly every expert's rows (expert counts spread
-    // around their mean); experts with many more rows run faster in 192-row tiles. (The
-    // 256-row gate|up kernel, with its bf16 operands widened in registers, spills; it remains
-    // for the flag only.)
-    if (per < 150 || per > 256) return TileShape::Rows192;
-    return TileShape::Rows224;
+    // Above that, the height whose tiles the experts' rows fill best: a tile costs its
+    // expert's whole weight stream however few rows it holds, and the 224-row kernel does
+    // more work per cycle than the 192-row one. Measured at K2 shapes (uniform top-8 routing
+    // over 384 experts, 3,072-24,576 tokens), the fastest height was:
+    //   128 up to about 107 rows per expert (one tile each);
+    //   224 from 112 to 213 (one tile each; 2-4% faster than 192);
+    //   128 from 224 to 256 (two full tiles; 224 leaves a second, nearly empty tile);
+    //   192 from 267 to 320, 224 at 427, 192 at 512 and above (the shard's 1,365).
+    // (The 256-row gate|up kernel, with its bf16 operands widened in registers, spills; it
+    // remains for the flag only.)
+    if (per < 110) return TileShape::Rows128;
+    if (per < 220) return TileShape::Rows224;
+    if (per < 262) return TileShape::Rows128;
+    if (per < 380) return TileShape::Rows192;
+    if (per < 460) return TileShape::Rows224;
+    return TileShape::Rows192;
 }
 
 }  // namespace

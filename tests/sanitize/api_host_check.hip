@@ -72,6 +72,7 @@ struct Region {
 };
 static std::vector<Region> g_regions;
 static int g_launches = 0;
+static int g_gate_up_rows = -1;   // tile height of the last gate|up launch
 static volatile uint8_t g_sink;
 
 static void rd(const char* name, const void* p, size_t n) {
@@ -153,8 +154,9 @@ hipError_t launch_build_tiles(const int32_t* offsets, int E, int64_t, int, int64
     return hipSuccess;
 }
 
-hipError_t launch_gate_up(const GateUpArgs& a, TileShape, hipStream_t) {
+hipError_t launch_gate_up(const GateUpArgs& a, TileShape shape, hipStream_t) {
     ++g_launches;
+    g_gate_up_rows = tile_rows(shape);
     rd("xq", a.xq, (size_t)a.N * a.d);
     rd("xs", a.xs, (size_t)a.N * (a.d / kGroup) * 4);
     rd("sorted_slot", a.sorted_slot, (size_t)a.rows * 4);
@@ -447,6 +449,34 @@ static void size_queries() {
     CHECK(moe_swiglu_workspace_size(4, 9, 8, 128, 128) == 0, "swiglu ws, K > E");
 }
 
+// The automatic tile height against the expected rows per touched expert (K = 1 over E = 8
+// experts, so N = 8 per): the measured bands -- 16 rows below 6 per expert, then 128, 224,
+// 128, 192, 224 and 192 with edges at 110, 220, 262, 380 and 460 -- on both sides of each edge.
+static void tile_rule() {
+    struct Case {
+        int64_t N;
+        int rows;
+    };
+    const Case cases[] = {{4, 16},      {40, 16},     {48, 128},    {872, 128},   {880, 224},  {1752, 224},
+                          {1760, 128},  {2088, 128},  {2096, 192},  {3032, 192},  {3040, 224}, {3672, 224},
+                          {3680, 192},  {10920, 192}};
+    const int32_t E = 8, d = 128, F = 128;
+    for (const Case& c : cases) {
+        const int64_t N = c.N;
+        Buf x(N * d * 2), offsets((E + 1) * 4), sorted(N * 4), y(N * d * 2);
+        Buf wg((size_t)E * F * d), wu(wg.n), wd(wg.n), sg((size_t)E * 4), su(sg.n), sd(sg.n);
+        Buf ws(moe_swiglu_workspace_size(N, 1, E, d, F));
+        begin();
+        g_gate_up_rows = -1;
+        const moe_status st = moe_grouped_swiglu(x.as<uint16_t>(), N, 1, E, d, F, offsets.as<int32_t>(),
+                                                 sorted.as<int32_t>(), wg.as<uint8_t>(), sg.as<float>(),
+                                                 wu.as<uint8_t>(), su.as<float>(), wd.as<uint8_t>(), sd.as<float>(),
+                                                 y.as<uint16_t>(), ws.p, ws.n, 0, nullptr);
+        CHECK(st == MOE_OK && g_gate_up_rows == c.rows, "N=%lld (%.1f rows per expert): %d-row tiles, want %d",
+              (long long)N, N / 8.0, g_gate_up_rows, c.rows);
+    }
+}
+
 int main() {
     // no device: a valid call reports the HIP error
     {
@@ -476,6 +506,7 @@ int main() {
         {40, 12, 16, 1536, 256},  // K = 12
     };
     for (const Shape& sh : shapes) valid_calls(sh);
+    tile_rule();
     // checked dispatch reports what the device-side check found
     {
         const int64_t N = 6;

@@ -270,7 +270,7 @@ def measure(cfg, args, dev, graph: bool):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8-e4m3 x fp8-e4m3 -> fp32 (bf16 in/out)",
+        "dtype": "fp8-e4m3 x fp8-e4m3 -> fp32 (gate|up block sums on bf16 matrix ops, exact for e4m3 codes; down on fp8 ones; bf16 in/out)",
         "data": "synthetic (seeded; random-init fp8 expert weights, 128x128 block scales)",
         "config": {"workload": cfg.name, "tile": args.tile, "tokens": cfg.layer_tokens, "rows": N * K, "d": d,
                    "d_ff": d_ff, "experts": E, "top_k": K, "shared_expert": bool(cfg.shared),

@@ -22,10 +22,12 @@
 //
 // Operands: each weight byte is needed by one wave only, and the tile's few token
 // rows (16) are read by every wave from L2, so both go straight from memory into
-// the MFMA operand registers, one K block ahead of use, in two register sets used
-// in turn: a wave never waits for the block it has just asked for, and no barrier
-// couples the waves inside the K loop. (Staging the token rows through LDS made
-// every K block end in a full wait for the next block's loads and a barrier.)
+// registers, one K block ahead of use, in two register sets used in turn: a wave
+// never waits for the block it has just asked for, and no barrier couples the waves
+// inside the K loop. (Staging the token rows through LDS made every K block end in a
+// full wait for the next block's loads and a barrier.) The weights are read as whole
+// cache lines with the nontemporal hint and moved into the operand layout by DPP
+// (load_frag_lines below).
 //
 // Any 16x16x128 operand layout works as long as A and B use the same one: lane l
 // supplies row (l & 15) and the 32 K-values [32*(l>>4), 32*(l>>4)+32) of its

@@ -49,10 +49,12 @@ _WS_RETIRED: list = []
 
 
 def _workspace(nbytes: int, dev: torch.device, tag: str) -> torch.Tensor:
-    """A cached uint8 workspace per (device, purpose), grown as needed. Calls that use the
-    same workspace are ordered on the current stream. A workspace that is outgrown stays
-    allocated: a captured HIP graph may still address it."""
-    key = (str(dev), tag)
+    """A cached uint8 workspace per (device, stream, purpose), grown as needed. Calls on one
+    stream run in order, so they can share it; calls on different streams get workspaces of
+    their own and may overlap. (A graph capture runs on a stream of its own, so its first call
+    allocates inside the capture, from the graph's memory pool.) A workspace that is outgrown
+    stays allocated: a captured HIP graph may still address it."""
+    key = (str(dev), torch.cuda.current_stream(dev).cuda_stream, tag)
     ws = _WS_CACHE.get(key)
     if ws is None or ws.numel() < nbytes:
         if ws is not None:

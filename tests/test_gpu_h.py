@@ -47,7 +47,7 @@ TILE_IDS = ["auto", "16", "128", "192", "224", "256"]
 def _gpu_h(xq, xs, disp, exd, flags, rows, d_ff):
     moe.grouped_swiglu_q(xq, xs, disp, exd, flags, _ws_tag="h_check")
     torch.cuda.synchronize()
-    ws = api._WS_CACHE[(str(xq.device), "h_check")].cpu().numpy()
+    ws = api._WS_CACHE[(str(xq.device), torch.cuda.current_stream(xq.device).cuda_stream, "h_check")].cpu().numpy()
     hq = ws[:rows * d_ff].reshape(rows, d_ff).copy()
     off = (rows * d_ff + 255) // 256 * 256
     hs = ws[off:off + rows * (d_ff // 128) * 4].view(np.float32).reshape(rows, d_ff // 128).copy()
